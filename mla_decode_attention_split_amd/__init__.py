@@ -1,0 +1,191 @@
+"""Paged MLA decode with split-KV on MI355X (gfx950).
+
+Thin binding over ``libmla_decode.so`` (C ABI in ``include/mla_decode.h``):
+argument marshalling only -- every step of the decode runs in the library's
+HIP kernels.  PyTorch provides device memory and the current stream.
+
+Entry points with the C names: :func:`mla_get_metadata_shape`,
+:func:`mla_get_metadata`, :func:`mla_decode_workspace_size`,
+:func:`mla_decode`.  The two calls the pages show ("DeepSeek 开源记-第1天-
+FlashMLA", section 6) are :func:`get_mla_metadata` and
+:func:`flash_mla_with_kvcache`, with the same argument order.
+
+If the library is missing or cannot be loaded, every call raises: there is no
+fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = [
+    "MlaError", "library_path", "mla_get_metadata_shape", "mla_get_metadata",
+    "mla_decode_workspace_size", "mla_decode", "get_mla_metadata", "flash_mla_with_kvcache",
+    "HEAD_DIM", "VALUE_DIM", "PAGE_SIZE",
+]
+
+HEAD_DIM = 576
+VALUE_DIM = 512
+PAGE_SIZE = 64
+METADATA_WORDS = 8
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libmla_decode.so")
+_lib = None
+
+
+class MlaError(RuntimeError):
+    """A nonzero status from the C library (message from mla_last_error)."""
+
+    def __init__(self, status: int, message: str):
+        super().__init__(f"[{status}] {message}")
+        self.status = status
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise MlaError(-4, f"{_LIB_PATH} is missing: build it with "
+                           "`python -m mla_decode_attention_split_amd.build`")
+    lib = ctypes.CDLL(_LIB_PATH)
+    i, p, sz = ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t
+    lib.mla_status_string.argtypes = [i]
+    lib.mla_status_string.restype = ctypes.c_char_p
+    lib.mla_last_error.argtypes = []
+    lib.mla_last_error.restype = ctypes.c_char_p
+    lib.mla_get_metadata_shape.argtypes = [i, i, i, ctypes.POINTER(i), ctypes.POINTER(i),
+                                           ctypes.POINTER(i)]
+    lib.mla_get_metadata_shape.restype = i
+    lib.mla_get_metadata.argtypes = [p, i, i, i, i, i, p, p, p]
+    lib.mla_get_metadata.restype = i
+    lib.mla_decode_workspace_size.argtypes = [i, i, i, i]
+    lib.mla_decode_workspace_size.restype = sz
+    lib.mla_decode.argtypes = [p, p, p, p, i, i, i, i, i, i, i, i, i, p, i, p, i, ctypes.c_float,
+                               p, p, p, sz, p]
+    lib.mla_decode.restype = i
+    _lib = lib
+    return lib
+
+
+def _check(status: int):
+    if status != 0:
+        lib = _load()
+        raise MlaError(status, (lib.mla_last_error() or lib.mla_status_string(status)).decode())
+
+
+def _stream_of(device):
+    import torch
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def mla_get_metadata_shape(batch: int, q_rows_per_kv_head: int, h_kv: int):
+    """Returns ``(num_parts, fixed_cost, tile_rows)`` for the current device."""
+    lib = _load()
+    n, f, t = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
+    _check(lib.mla_get_metadata_shape(int(batch), int(q_rows_per_kv_head), int(h_kv),
+                                      ctypes.byref(n), ctypes.byref(f), ctypes.byref(t)))
+    return n.value, f.value, t.value
+
+
+def mla_get_metadata(cache_seqlens, q_rows_per_kv_head: int, h_kv: int, *,
+                     num_parts: int | None = None, fixed_cost: int | None = None):
+    """Split-KV scheduling metadata on the device of ``cache_seqlens``.
+
+    Returns ``(tile_metadata int32 [num_parts, 8], num_splits int32 [B+1])``;
+    ``num_parts`` / ``fixed_cost`` default to :func:`mla_get_metadata_shape`.
+    """
+    import torch
+    if cache_seqlens.dtype != torch.int32 or not cache_seqlens.is_cuda or cache_seqlens.dim() != 1:
+        raise ValueError("cache_seqlens must be a 1-D int32 CUDA tensor")
+    seqlens = cache_seqlens.contiguous()
+    batch = seqlens.shape[0]
+    with torch.cuda.device(seqlens.device):
+        dn, df, _ = mla_get_metadata_shape(batch, q_rows_per_kv_head, h_kv)
+        num_parts = dn if num_parts is None else int(num_parts)
+        fixed_cost = df if fixed_cost is None else int(fixed_cost)
+        meta = torch.empty((num_parts, METADATA_WORDS), dtype=torch.int32, device=seqlens.device)
+        splits = torch.empty((batch + 1,), dtype=torch.int32, device=seqlens.device)
+        _check(_load().mla_get_metadata(seqlens.data_ptr(), batch, int(q_rows_per_kv_head),
+                                        int(h_kv), num_parts, fixed_cost, meta.data_ptr(),
+                                        splits.data_ptr(), _stream_of(seqlens.device)))
+    return meta, splits
+
+
+def mla_decode_workspace_size(batch: int, q_rows_per_kv_head: int, h_kv: int,
+                              num_parts: int) -> int:
+    return int(_load().mla_decode_workspace_size(int(batch), int(q_rows_per_kv_head), int(h_kv),
+                                                 int(num_parts)))
+
+
+def mla_decode(q, blocked_k, block_table, cache_seqlens, tile_metadata, num_splits, *,
+               causal: bool = False, softmax_scale: float | None = None, out=None, lse=None,
+               workspace=None):
+    """Paged MLA decode.  ``q`` bf16 [B, s_q, h_q, 576]; ``blocked_k`` bf16
+    [num_pages, 64, h_kv, 576]; ``block_table`` int32 [B, max_blocks];
+    ``cache_seqlens`` int32 [B].  Returns ``(out bf16 [B, s_q, h_q, 512],
+    lse fp32 [B, s_q, h_q])``."""
+    import torch
+    if q.dtype != torch.bfloat16 or blocked_k.dtype != torch.bfloat16:
+        raise ValueError("q and blocked_k must be bfloat16")
+    if block_table.dtype != torch.int32 or cache_seqlens.dtype != torch.int32:
+        raise ValueError("block_table and cache_seqlens must be int32")
+    if tile_metadata.dtype != torch.int32 or num_splits.dtype != torch.int32:
+        raise ValueError("tile_metadata and num_splits must be int32")
+    for name, t in (("q", q), ("blocked_k", blocked_k), ("block_table", block_table),
+                    ("cache_seqlens", cache_seqlens), ("tile_metadata", tile_metadata),
+                    ("num_splits", num_splits)):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous CUDA tensor")
+    if q.dim() != 4 or blocked_k.dim() != 4 or block_table.dim() != 2:
+        raise ValueError("q [B,s_q,h_q,d], blocked_k [P,page,h_kv,d], block_table [B,n] expected")
+    B, s_q, h_q, d = q.shape
+    num_pages, page, h_kv, d2 = blocked_k.shape
+    if d2 != d:
+        raise ValueError("q and blocked_k disagree on the head dim")
+    if block_table.shape[0] != B or cache_seqlens.shape != (B,):
+        raise ValueError("block_table / cache_seqlens batch mismatch")
+    if tile_metadata.dim() != 2 or tile_metadata.shape[1] != METADATA_WORDS:
+        raise ValueError("tile_metadata must be [num_parts, 8]")
+    if num_splits.shape != (B + 1,):
+        raise ValueError("num_splits must be [B+1]")
+    num_parts = tile_metadata.shape[0]
+    scale = float(d) ** -0.5 if softmax_scale is None else float(softmax_scale)
+    dev = q.device
+    M = s_q * h_q // max(h_kv, 1)
+    with torch.cuda.device(dev):
+        if out is None:
+            out = torch.empty((B, s_q, h_q, VALUE_DIM), dtype=torch.bfloat16, device=dev)
+        if lse is None:
+            lse = torch.empty((B, s_q, h_q), dtype=torch.float32, device=dev)
+        need = mla_decode_workspace_size(B, M, h_kv, num_parts) if h_q % max(h_kv, 1) == 0 else 0
+        if workspace is None:
+            workspace = torch.empty((max(need, 16),), dtype=torch.uint8, device=dev)
+        _check(_load().mla_decode(
+            q.data_ptr(), blocked_k.data_ptr(), block_table.data_ptr(), cache_seqlens.data_ptr(),
+            B, s_q, h_q, h_kv, d, VALUE_DIM, num_pages, page, block_table.shape[1],
+            tile_metadata.data_ptr(), num_parts, num_splits.data_ptr(), int(bool(causal)), scale,
+            out.data_ptr(), lse.data_ptr(), workspace.data_ptr(),
+            workspace.numel() * workspace.element_size(), _stream_of(dev)))
+    return out, lse
+
+
+def get_mla_metadata(cache_seqlens, num_heads_per_head_k: int, num_heads_k: int):
+    """The pages' metadata call: ``get_mla_metadata(cache_seqlens,
+    s_q * h_q // h_kv, h_kv)`` -> ``(tile_scheduler_metadata, num_splits)``."""
+    return mla_get_metadata(cache_seqlens, num_heads_per_head_k, num_heads_k)
+
+
+def flash_mla_with_kvcache(q, k_cache, block_table, cache_seqlens, head_dim_v: int,
+                           tile_scheduler_metadata, num_splits, softmax_scale=None,
+                           causal: bool = False):
+    """The pages' decode call; returns ``(output, lse)``."""
+    if head_dim_v != VALUE_DIM:
+        raise MlaError(-2, f"value dim {head_dim_v} (only {VALUE_DIM})")
+    return mla_decode(q, k_cache, block_table, cache_seqlens, tile_scheduler_metadata, num_splits,
+                      causal=causal, softmax_scale=softmax_scale)

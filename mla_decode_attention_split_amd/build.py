@@ -1,0 +1,58 @@
+"""Build libmla_decode.so in-tree with hipcc for gfx950.
+
+Usage: ``python -m mla_decode_attention_split_amd.build`` (or call
+:func:`build`).  Every HIP source is compiled with packed-fp32 instructions
+disabled and linked into one shared library next to this file.
+"""
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+from concurrent.futures import ThreadPoolExecutor
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(HERE, "csrc")
+LIB = os.path.join(HERE, "libmla_decode.so")
+SOURCES = ["api.hip", "sched.hip", "decode.hip", "combine.hip"]
+ARCH = os.environ.get("MLA_OFFLOAD_ARCH", "gfx950")
+
+COMMON = [
+    "--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wall", "-Wno-unused-function",
+]
+
+
+def _run(cmd):
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    # hipcc's host pass does not know the packed-fp32 target feature; drop that notice
+    noise = "'-packed-fp32-ops' is not a recognized feature"
+    err = "\n".join(l for l in r.stderr.splitlines() if noise not in l)
+    if r.returncode != 0:
+        raise RuntimeError(f"command failed: {' '.join(cmd)}\n{err}")
+    if err.strip():
+        print(err, file=sys.stderr)
+
+
+def build(verbose: bool = False) -> str:
+    objdir = os.path.join(HERE, "_build")
+    os.makedirs(objdir, exist_ok=True)
+    objs = []
+    cmds = []
+    for s in SOURCES:
+        obj = os.path.join(objdir, s.replace(".hip", ".o"))
+        objs.append(obj)
+        cmds.append(["hipcc", *COMMON, "-c", os.path.join(CSRC, s), "-o", obj])
+    with ThreadPoolExecutor(max_workers=min(4, os.cpu_count() or 1)) as ex:
+        list(ex.map(_run, cmds))
+    tmp = LIB + ".tmp"
+    _run(["hipcc", "--offload-arch=" + ARCH, "-shared", "-fPIC", *objs, "-o", tmp])
+    os.replace(tmp, LIB)
+    if verbose:
+        print("built", LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    build(verbose=True)

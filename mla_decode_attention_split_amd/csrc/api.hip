@@ -1,0 +1,222 @@
+// C ABI of libmla_decode.so: argument checks, sizing and kernel dispatch.
+// Declarations and the contract of every entry point: include/mla_decode.h.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <mutex>
+
+#include "../../include/mla_decode.h"
+#include "mla_common.hpp"
+#include "mla_internal.hpp"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+int ok() {
+  g_err[0] = '\0';
+  return MLA_OK;
+}
+
+// Compute-unit count per device, read once.
+constexpr int kMaxDevices = 64;
+int g_cus[kMaxDevices];
+std::once_flag g_cu_once[kMaxDevices];
+
+int device_cus(int* cus) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(MLA_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(MLA_ERR_UNSUPPORTED, "device index %d", dev);
+  hipError_t err = hipSuccess;
+  std::call_once(g_cu_once[dev], [&]() {
+    int n = 0;
+    err = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+    g_cus[dev] = n > 0 ? n : 256;
+  });
+  if (err != hipSuccess)
+    return fail(MLA_ERR_HIP, "hipDeviceGetAttribute: %s", hipGetErrorString(err));
+  *cus = g_cus[dev];
+  return MLA_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int check_rows(int q_rows_per_kv_head, int h_kv) {
+  if (q_rows_per_kv_head < 1 || q_rows_per_kv_head > MLA_MAX_ROWS)
+    return fail(MLA_ERR_UNSUPPORTED, "rows per KV head %d outside [1, %d]", q_rows_per_kv_head,
+                MLA_MAX_ROWS);
+  if (h_kv < 1 || h_kv > 1024) return fail(MLA_ERR_INVALID_ARG, "h_kv %d outside [1, 1024]", h_kv);
+  return MLA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* mla_status_string(int status) {
+  switch (status) {
+    case MLA_OK: return "ok";
+    case MLA_ERR_INVALID_ARG: return "invalid argument";
+    case MLA_ERR_UNSUPPORTED: return "unsupported configuration";
+    case MLA_ERR_WORKSPACE: return "workspace too small";
+    case MLA_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char* mla_last_error(void) { return g_err; }
+
+int mla_get_metadata_shape(int batch, int q_rows_per_kv_head, int h_kv, int* num_parts,
+                           int* fixed_cost, int* tile_rows) {
+  if (batch < 1 || batch > MLA_MAX_BATCH)
+    return fail(MLA_ERR_INVALID_ARG, "batch %d outside [1, %d]", batch, MLA_MAX_BATCH);
+  int rc = check_rows(q_rows_per_kv_head, h_kv);
+  if (rc != MLA_OK) return rc;
+  int cus = 0;
+  rc = device_cus(&cus);
+  if (rc != MLA_OK) return rc;
+  const int tr = mla::tile_rows_for(q_rows_per_kv_head);
+  const int m_tiles = (q_rows_per_kv_head + tr - 1) / tr;
+  // One workgroup per compute unit: parts x row tiles x KV heads ~ CUs,
+  // rounded down to a multiple of 8 so each part's tiles share an XCD.
+  int parts = cus / (m_tiles * h_kv);
+  parts = parts >= 8 ? (parts / 8) * 8 : 8;
+  if (num_parts) *num_parts = parts;
+  // Per-sequence overhead in 32-key units: query load, epilogue and the
+  // combine of one more piece.
+  if (fixed_cost) *fixed_cost = 2 + tr / 64;
+  if (tile_rows) *tile_rows = tr;
+  return ok();
+}
+
+int mla_get_metadata(const int32_t* cache_seqlens, int batch, int q_rows_per_kv_head, int h_kv,
+                     int num_parts, int fixed_cost, int32_t* tile_metadata, int32_t* num_splits,
+                     void* stream) {
+  if (batch < 1 || batch > MLA_MAX_BATCH)
+    return fail(MLA_ERR_INVALID_ARG, "batch %d outside [1, %d]", batch, MLA_MAX_BATCH);
+  int rc = check_rows(q_rows_per_kv_head, h_kv);
+  if (rc != MLA_OK) return rc;
+  if (num_parts < 1 || num_parts > MLA_MAX_PARTS)
+    return fail(MLA_ERR_INVALID_ARG, "num_parts %d outside [1, %d]", num_parts, MLA_MAX_PARTS);
+  if (fixed_cost < 1) return fail(MLA_ERR_INVALID_ARG, "fixed_cost %d < 1", fixed_cost);
+  if (!cache_seqlens || !tile_metadata || !num_splits)
+    return fail(MLA_ERR_INVALID_ARG, "null pointer (cache_seqlens, tile_metadata, num_splits)");
+  if (!aligned16(tile_metadata)) return fail(MLA_ERR_INVALID_ARG, "tile_metadata not 16-byte aligned");
+  hipError_t e = mla::launch_sched(cache_seqlens, batch, num_parts, fixed_cost, tile_metadata,
+                                   num_splits, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(MLA_ERR_HIP, "scheduler launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+size_t mla_decode_workspace_size(int batch, int q_rows_per_kv_head, int h_kv, int num_parts) {
+  if (batch < 1 || batch > MLA_MAX_BATCH || q_rows_per_kv_head < 1 ||
+      q_rows_per_kv_head > MLA_MAX_ROWS || h_kv < 1 || num_parts < 1 || num_parts > MLA_MAX_PARTS)
+    return 0;
+  const size_t pieces = (size_t)batch + (size_t)num_parts;
+  const size_t rows = pieces * (size_t)h_kv * (size_t)q_rows_per_kv_head;
+  size_t o_bytes = rows * MLA_VALUE_DIM * sizeof(float);
+  size_t l_bytes = rows * sizeof(float);
+  l_bytes = (l_bytes + 255) & ~(size_t)255;
+  return o_bytes + l_bytes;
+}
+
+int mla_decode(const void* q, const void* blocked_k, const int32_t* block_table,
+               const int32_t* cache_seqlens, int batch, int s_q, int h_q, int h_kv, int d, int dv,
+               int num_pages, int page_size, int max_blocks_per_seq,
+               const int32_t* tile_metadata, int num_parts, const int32_t* num_splits, int causal,
+               float softmax_scale, void* out, float* lse, void* workspace,
+               size_t workspace_bytes, void* stream) {
+  if (d != MLA_HEAD_DIM) return fail(MLA_ERR_UNSUPPORTED, "head dim %d (only %d)", d, MLA_HEAD_DIM);
+  if (dv != MLA_VALUE_DIM)
+    return fail(MLA_ERR_UNSUPPORTED, "value dim %d (only %d)", dv, MLA_VALUE_DIM);
+  if (page_size != MLA_PAGE_SIZE)
+    return fail(MLA_ERR_UNSUPPORTED, "page size %d (only %d)", page_size, MLA_PAGE_SIZE);
+  if (batch < 1 || batch > MLA_MAX_BATCH)
+    return fail(MLA_ERR_INVALID_ARG, "batch %d outside [1, %d]", batch, MLA_MAX_BATCH);
+  if (s_q < 1 || h_q < 1 || h_kv < 1 || h_q % h_kv != 0)
+    return fail(MLA_ERR_INVALID_ARG, "s_q %d, h_q %d, h_kv %d (need h_q %% h_kv == 0)", s_q, h_q,
+                h_kv);
+  const long long M_ll = (long long)s_q * (h_q / h_kv);
+  if (M_ll > MLA_MAX_ROWS)
+    return fail(MLA_ERR_UNSUPPORTED, "s_q * h_q / h_kv = %lld > %d", M_ll, MLA_MAX_ROWS);
+  const int M = (int)M_ll;
+  int rc = check_rows(M, h_kv);
+  if (rc != MLA_OK) return rc;
+  if (num_pages < 1 || max_blocks_per_seq < 1)
+    return fail(MLA_ERR_INVALID_ARG, "num_pages %d, max_blocks_per_seq %d", num_pages,
+                max_blocks_per_seq);
+  if (num_parts < 1 || num_parts > MLA_MAX_PARTS)
+    return fail(MLA_ERR_INVALID_ARG, "num_parts %d outside [1, %d]", num_parts, MLA_MAX_PARTS);
+  if (!std::isfinite(softmax_scale))
+    return fail(MLA_ERR_INVALID_ARG, "softmax_scale is not finite");
+  if (!q || !blocked_k || !block_table || !cache_seqlens || !tile_metadata || !num_splits || !out ||
+      !lse || !workspace)
+    return fail(MLA_ERR_INVALID_ARG, "null pointer argument");
+  if (!aligned16(q) || !aligned16(blocked_k) || !aligned16(out) || !aligned16(workspace))
+    return fail(MLA_ERR_INVALID_ARG, "q, blocked_k, out and workspace must be 16-byte aligned");
+  const size_t need = mla_decode_workspace_size(batch, M, h_kv, num_parts);
+  if (workspace_bytes < need)
+    return fail(MLA_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", workspace_bytes, need);
+
+  const int tr = mla::tile_rows_for(M);
+  const size_t pieces = (size_t)batch + (size_t)num_parts;
+  const size_t rows = pieces * (size_t)h_kv * (size_t)M;
+
+  mla::DecodeArgs a;
+  a.q = static_cast<const uint16_t*>(q);
+  a.kv = static_cast<const uint16_t*>(blocked_k);
+  a.block_table = block_table;
+  a.seqlens = cache_seqlens;
+  a.meta = tile_metadata;
+  a.num_splits = num_splits;
+  a.out = static_cast<uint16_t*>(out);
+  a.lse = lse;
+  a.o_part = static_cast<float*>(workspace);
+  a.lse_part = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                        rows * MLA_VALUE_DIM * sizeof(float));
+  a.batch = batch;
+  a.s_q = s_q;
+  a.h_q = h_q;
+  a.h_kv = h_kv;
+  a.M = M;
+  a.max_blocks = max_blocks_per_seq;
+  a.num_parts = num_parts;
+  a.m_tiles = (M + tr - 1) / tr;
+  a.causal = causal ? 1 : 0;
+  a.xcd_map = (num_parts % 8 == 0) ? 1 : 0;
+  a.scale_log2 = softmax_scale * 1.44269504088896340736f;
+  const long long grid = (long long)num_parts * a.m_tiles * h_kv;
+  if (grid > 0x7fffffffLL) return fail(MLA_ERR_UNSUPPORTED, "grid too large");
+
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e = mla::launch_decode(a, tr, st);
+  if (e != hipSuccess) return fail(MLA_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
+
+  mla::CombineArgs c;
+  c.num_splits = num_splits;
+  c.o_part = a.o_part;
+  c.lse_part = a.lse_part;
+  c.out = a.out;
+  c.lse = lse;
+  c.batch = batch;
+  c.s_q = s_q;
+  c.h_q = h_q;
+  c.h_kv = h_kv;
+  c.M = M;
+  e = mla::launch_combine(c, st);
+  if (e != hipSuccess) return fail(MLA_ERR_HIP, "combine launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+}  // extern "C"

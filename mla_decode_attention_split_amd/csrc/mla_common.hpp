@@ -1,0 +1,75 @@
+// Shared device-side definitions of the paged MLA decode kernels (gfx950).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mla {
+
+// Fixed sizes (cnblogs FlashMLA notes, section 2: head dim 576, value dim 512;
+// ygpos news: paged cache with block size 64).
+constexpr int kHeadDim = 576;
+constexpr int kValueDim = 512;
+constexpr int kPage = 64;
+constexpr int kRowBytes = kHeadDim * 2;            // one cached bf16 row
+constexpr int kChunksPerRow = kRowBytes / 16;      // 72 chunks of 16 B
+
+// A stage is 32 consecutive keys of one sequence (half a page); sequences are
+// split only at stage boundaries.
+constexpr int kStage = 32;
+constexpr int kStageBytes = kStage * kRowBytes;    // 36864 B
+constexpr int kSlots = 4;                          // LDS ring of stages
+constexpr int kLdsBytes = kSlots * kStageBytes;    // 147456 B of 160 KB
+constexpr int kLoadsPerStage = kStageBytes / 1024; // 1 KB per wave-wide 16 B load
+constexpr int kWaves = 4;
+constexpr int kMetaWords = 8;
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+#define MLA_LDS __attribute__((address_space(3)))
+
+// XOR swizzle of the 16-byte chunk index inside each 128-byte group of a
+// cached row held in LDS.  Eight consecutive rows get eight distinct values
+// (conflict-free 16 B reads of one chunk across rows), and four consecutive
+// rows starting at a multiple of 4 map an aligned chunk pair to four
+// disjoint pairs (conflict-free transposed 8 B reads).
+__device__ __forceinline__ int swz(int row) { return 2 * (row & 3) + ((row >> 2) & 1); }
+
+__device__ __forceinline__ int phys_chunk(int row, int chunk) {
+  return (chunk & ~7) | ((chunk & 7) ^ swz(row));
+}
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Two floats -> packed bf16 pair (low half = lo), round to nearest even
+// (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
+}
+// The two floats a packed bf16 pair stands for.
+__device__ __forceinline__ float bf16_lo(uint32_t p) { return __uint_as_float(p << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t p) { return __uint_as_float(p & 0xffff0000u); }
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+// Waits and barriers written as asm so that the compiler neither moves memory
+// operations across them nor adds a full drain of the vector memory counter
+// (the prefetched stages must stay in flight across the barrier).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+__device__ __forceinline__ void wait_lgkm0() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+__device__ __forceinline__ void block_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+}  // namespace mla

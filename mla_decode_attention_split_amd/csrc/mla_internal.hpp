@@ -1,0 +1,45 @@
+// Host <-> kernel interface inside libmla_decode.so (not part of the C ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mla {
+
+constexpr int kMaxBatch = 16384;  // sequences per call (scheduler keeps prefix costs in LDS)
+
+struct DecodeArgs {
+  const uint16_t* q;          // bf16 [batch, s_q, h_q, 576]
+  const uint16_t* kv;         // bf16 [num_pages, 64, h_kv, 576]
+  const int32_t* block_table; // [batch, max_blocks]
+  const int32_t* seqlens;     // [batch]
+  const int32_t* meta;        // [num_parts, 8]
+  const int32_t* num_splits;  // [batch + 1]
+  uint16_t* out;              // bf16 [batch, s_q, h_q, 512]
+  float* lse;                 // [batch, s_q, h_q]
+  float* o_part;              // [max_pieces, h_kv, M, 512]
+  float* lse_part;            // [max_pieces, h_kv, M]
+  int batch, s_q, h_q, h_kv, M, max_blocks, num_parts, m_tiles;
+  int causal;
+  int xcd_map;                // 1: the m-tiles / KV heads of one part share an XCD
+  float scale_log2;           // softmax_scale * log2(e)
+};
+
+struct CombineArgs {
+  const int32_t* num_splits;
+  const float* o_part;
+  const float* lse_part;
+  uint16_t* out;
+  float* lse;
+  int batch, s_q, h_q, h_kv, M;
+};
+
+// Query rows per workgroup for M rows per KV head (16, 32, 64 or 128).
+inline int tile_rows_for(int M) { return M <= 16 ? 16 : M <= 32 ? 32 : M <= 64 ? 64 : 128; }
+
+hipError_t launch_sched(const int32_t* seqlens, int batch, int num_parts, int fixed_cost,
+                        int32_t* meta, int32_t* num_splits, hipStream_t stream);
+hipError_t launch_decode(const DecodeArgs& a, int tile_rows, hipStream_t stream);
+hipError_t launch_combine(const CombineArgs& a, hipStream_t stream);
+
+}  // namespace mla

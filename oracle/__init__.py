@@ -148,14 +148,15 @@ def decode_split(q, kcache, block_table, seqlens, cuts, *, causal: bool, scale: 
     return out, lse
 
 
-def schedule(seqlens, *, num_parts: int, fixed_cost: int, page_size: int = PAGE):
+def schedule(seqlens, *, num_parts: int, fixed_cost: int, unit_tokens: int = 32):
     """Split-KV partition: returns ``(tile_meta int32 [num_parts, 8],
-    num_splits int32 [B+1])`` following the rule written out in the C file."""
+    num_splits int32 [B+1])`` following the rule written out in the C file.
+    Sequences are cut only at multiples of ``unit_tokens`` keys."""
     seqlens = np.ascontiguousarray(seqlens, dtype=np.int32)
     B = seqlens.shape[0]
     meta = np.zeros((num_parts, 8), dtype=np.int32)
     splits = np.zeros(B + 1, dtype=np.int32)
-    rc = _load().mla_oracle_schedule(_ptr(seqlens), B, page_size, num_parts, fixed_cost,
+    rc = _load().mla_oracle_schedule(_ptr(seqlens), B, unit_tokens, num_parts, fixed_cost,
                                      _ptr(meta), _ptr(splits))
     if rc != 0:
         raise ValueError(f"mla_oracle_schedule failed with code {rc}")

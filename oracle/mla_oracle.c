@@ -260,35 +260,36 @@ int mla_oracle_decode_split(const uint16_t *q, const uint16_t *kcache, const int
  * Split-KV tile scheduling (the pages' block scheduling: the work is cut into
  * small blocks run in parallel, and get_mla_metadata returns
  * tile_scheduler_metadata and num_splits from cache_seqlens).  The pages give
- * no rule; this is the rule the library documents, written out step by step:
+ * no rule; this is the rule the library documents, written out step by step.
+ * A "unit" is unit_tokens consecutive keys of one sequence.
  *
- *   1. R_b = ceil(N_b / page_size) pages; cost_b = R_b + fixed_cost.
+ *   1. U_b = ceil(N_b / unit_tokens) units; cost_b = U_b + fixed_cost.
  *   2. C_b = cost_0 + ... + cost_{b-1};  total = C_B;
- *      T = ceil(total / num_parts)  (cost units per part).
- *   3. Part p owns the cost interval [p*T, (p+1)*T).  Page i of sequence b
+ *      T = ceil(total / num_parts)  (cost per part).
+ *   3. Part p owns the cost interval [p*T, (p+1)*T).  Unit i of sequence b
  *      sits at cost C_b + fixed_cost + i, so it belongs to part
- *      floor((C_b + fixed_cost + i) / T).  A sequence with no page gets one
+ *      floor((C_b + fixed_cost + i) / T).  A sequence with no unit gets one
  *      empty piece in part floor((C_b + fixed_cost - 1) / T).
- *   4. A piece is the run of one sequence's pages inside one part; pieces of
+ *   4. A piece is the run of one sequence's units inside one part; pieces of
  *      a sequence sit in consecutive parts.  num_splits[b+1] - num_splits[b]
  *      is the number of pieces of sequence b (num_splits[0] = 0).
- *   5. Per part p, 8 int32 words: first sequence, its first page, last
- *      sequence, its end page (exclusive), the split index of the first
- *      sequence's piece, then three zero words.  A part with no piece stores
- *      first = 0, last = -1.
+ *   5. Per part p, 8 int32 words: first sequence, first key of its piece,
+ *      last sequence, end key (exclusive, at most N) of its piece, the split
+ *      index of the first sequence's piece, then three zero words.  A part
+ *      with no piece stores first = 0, last = -1.
  */
-int mla_oracle_schedule(const int32_t *seqlens, int B, int page_size, int num_parts,
+int mla_oracle_schedule(const int32_t *seqlens, int B, int unit_tokens, int num_parts,
                         int fixed_cost, int32_t *tile_meta, int32_t *num_splits) {
-  if (B < 0 || page_size < 1 || num_parts < 1 || fixed_cost < 1) return ORACLE_ERR_ARG;
+  if (B < 0 || unit_tokens < 1 || num_parts < 1 || fixed_cost < 1) return ORACLE_ERR_ARG;
   long *C = (long *)malloc(sizeof(long) * (size_t)(B + 1));
   long *first = (long *)malloc(sizeof(long) * (size_t)(B > 0 ? B : 1));
   long *last = (long *)malloc(sizeof(long) * (size_t)(B > 0 ? B : 1));
-  long *pages = (long *)malloc(sizeof(long) * (size_t)(B > 0 ? B : 1));
-  if (!C || !first || !last || !pages) {
+  long *units = (long *)malloc(sizeof(long) * (size_t)(B > 0 ? B : 1));
+  if (!C || !first || !last || !units) {
     free(C);
     free(first);
     free(last);
-    free(pages);
+    free(units);
     return ORACLE_ERR_NOMEM;
   }
   C[0] = 0;
@@ -297,20 +298,20 @@ int mla_oracle_schedule(const int32_t *seqlens, int B, int page_size, int num_pa
       free(C);
       free(first);
       free(last);
-      free(pages);
+      free(units);
       return ORACLE_ERR_ARG;
     }
-    pages[b] = ((long)seqlens[b] + page_size - 1) / page_size;
-    C[b + 1] = C[b] + pages[b] + fixed_cost;
+    units[b] = ((long)seqlens[b] + unit_tokens - 1) / unit_tokens;
+    C[b + 1] = C[b] + units[b] + fixed_cost;
   }
   long total = C[B];
   long T = (total + num_parts - 1) / num_parts;
   if (T < 1) T = 1;
   num_splits[0] = 0;
   for (int b = 0; b < B; ++b) {
-    if (pages[b] > 0) {
+    if (units[b] > 0) {
       first[b] = (C[b] + fixed_cost) / T;
-      last[b] = (C[b] + fixed_cost + pages[b] - 1) / T;
+      last[b] = (C[b] + fixed_cost + units[b] - 1) / T;
     } else {
       first[b] = last[b] = (C[b] + fixed_cost - 1) / T;
     }
@@ -331,24 +332,26 @@ int mla_oracle_schedule(const int32_t *seqlens, int B, int page_size, int num_pa
       w[2] = -1;
       continue;
     }
-    long pg_begin = 0, pg_end = 0;
-    if (pages[bb] > 0) {
-      pg_begin = (long)p * T - C[bb] - fixed_cost;
-      if (pg_begin < 0) pg_begin = 0;
+    long u_begin = 0, u_end = 0;
+    if (units[bb] > 0) {
+      u_begin = (long)p * T - C[bb] - fixed_cost;
+      if (u_begin < 0) u_begin = 0;
     }
-    if (pages[be] > 0) {
-      pg_end = (long)(p + 1) * T - C[be] - fixed_cost;
-      if (pg_end > pages[be]) pg_end = pages[be];
+    if (units[be] > 0) {
+      u_end = (long)(p + 1) * T - C[be] - fixed_cost;
+      if (u_end > units[be]) u_end = units[be];
     }
+    long tok_end = u_end * unit_tokens;
+    if (tok_end > seqlens[be]) tok_end = seqlens[be];
     w[0] = bb;
-    w[1] = (int32_t)pg_begin;
+    w[1] = (int32_t)(u_begin * unit_tokens);
     w[2] = be;
-    w[3] = (int32_t)pg_end;
+    w[3] = (int32_t)tok_end;
     w[4] = (int32_t)(p - first[bb]);
   }
   free(C);
   free(first);
   free(last);
-  free(pages);
+  free(units);
   return ORACLE_OK;
 }

@@ -1,0 +1,176 @@
+"""GPU parity: the HIP path (through the C ABI binding) against the CPU oracle.
+
+Every case prints its name and shape before touching the GPU.  Tolerances
+are in tests/parity.py.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from mla_decode_attention_split_amd import synth
+from parity import bf16_bits_of, check_parity, log, run_gpu, subset, to_device
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu_ready():
+    import torch
+    assert torch.cuda.is_available(), "the gpu tests need an MI355X"
+    import mla_decode_attention_split_amd as mla
+    mla._load()  # raises if the HIP library is missing
+
+
+def ref(w):
+    return oracle.decode(w.q, w.kcache, w.block_table, w.seqlens, causal=w.causal, scale=w.scale)
+
+
+def case(w, what):
+    log(f"[case] {what}: B={w.batch} s_q={w.s_q} h_q={w.h_q} h_kv={w.h_kv} causal={w.causal} "
+        f"N={list(map(int, w.seqlens))[:8]}{'...' if w.batch > 8 else ''}")
+
+
+def test_tiny_workload():
+    w = synth.named_workload("tiny")
+    case(w, "tiny")
+    out, lse = run_gpu(w)
+    check_parity(out, lse, *ref(w), what="tiny")
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_random_small_shapes(seed):
+    rng = np.random.default_rng(500 + seed)
+    B = int(rng.integers(1, 6))
+    s_q = int(rng.integers(1, 5))
+    h_q = int(rng.choice([16, 32, 64, 128]))
+    causal = bool(rng.integers(0, 2))
+    lens = rng.integers(0, 701, size=B)
+    w = synth.make_workload(lens, s_q=s_q, h_q=h_q, causal=causal, seed=seed,
+                            extra_pages=int(rng.integers(0, 4)))
+    case(w, f"random seed {seed}")
+    out, lse = run_gpu(w)
+    check_parity(out, lse, *ref(w), what=f"seed {seed}")
+
+
+@pytest.mark.parametrize("h_q,s_q", [(8, 1), (24, 1), (40, 1), (16, 3), (48, 3), (128, 3),
+                                     (96, 1), (16, 8)])
+def test_row_tile_boundaries(h_q, s_q):
+    w = synth.make_workload([130, 77, 300], s_q=s_q, h_q=h_q, causal=True, seed=h_q + s_q)
+    case(w, f"rows {s_q * h_q}")
+    out, lse = run_gpu(w)
+    check_parity(out, lse, *ref(w), what=f"M={s_q * h_q}")
+
+
+@pytest.mark.parametrize("s_q,causal", [(1, False), (2, True), (4, True)])
+def test_edge_lengths(s_q, causal):
+    lens = [0, 1, 2, 3, 31, 32, 33, 63, 64, 65, 127, 128, 129, 1000]
+    w = synth.make_workload(lens, s_q=s_q, h_q=16, causal=causal, seed=40 + s_q)
+    case(w, "edge lengths")
+    out, lse = run_gpu(w)
+    check_parity(out, lse, *ref(w), what=f"edge s_q={s_q}")
+
+
+def test_metadata_bitexact():
+    import mla_decode_attention_split_amd as mla
+    rng = np.random.default_rng(7)
+    import torch
+    for trial in range(12):
+        B = int(rng.integers(1, 300))
+        lens = rng.integers(0, 20000, size=B).astype(np.int32)
+        if trial % 3 == 0:
+            lens[rng.integers(0, B, size=max(1, B // 5))] = 0
+        num_parts = int(rng.choice([1, 7, 8, 64, 128, 256, 1000]))
+        fixed_cost = int(rng.integers(1, 8))
+        log(f"[case] metadata trial {trial}: B={B} parts={num_parts} fixed={fixed_cost}")
+        sl = torch.from_numpy(lens).cuda()
+        meta, splits = mla.mla_get_metadata(sl, 16, 1, num_parts=num_parts, fixed_cost=fixed_cost)
+        torch.cuda.synchronize()
+        rmeta, rsplits = oracle.schedule(lens, num_parts=num_parts, fixed_cost=fixed_cost,
+                                         unit_tokens=32)
+        np.testing.assert_array_equal(meta.cpu().numpy(), rmeta)
+        np.testing.assert_array_equal(splits.cpu().numpy(), rsplits)
+
+
+@pytest.mark.parametrize("num_parts", [1, 7, 64, None])
+def test_split_count_does_not_change_result(num_parts):
+    lens = [5000, 33, 1, 700, 64, 2048, 0, 3000]
+    w = synth.make_workload(lens, s_q=2, h_q=64, causal=True, seed=21)
+    case(w, f"num_parts={num_parts}")
+    out, lse = run_gpu(w, num_parts=num_parts)
+    check_parity(out, lse, *ref(w), what=f"parts={num_parts}")
+
+
+def test_deterministic_bitwise():
+    import torch
+    import mla_decode_attention_split_amd as mla
+    w = synth.make_workload([4000, 100, 2500], s_q=1, h_q=128, seed=22)
+    case(w, "determinism")
+    q, kv, bt, sl = to_device(w)
+    meta, splits = mla.mla_get_metadata(sl, w.rows_per_kv_head, 1)
+    o1, l1 = mla.mla_decode(q, kv, bt, sl, meta, splits, softmax_scale=w.scale)
+    o2, l2 = mla.mla_decode(q, kv, bt, sl, meta, splits, softmax_scale=w.scale)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(bf16_bits_of(o1), bf16_bits_of(o2))
+    np.testing.assert_array_equal(l1.cpu().numpy(), l2.cpu().numpy())
+
+
+def test_page_permutation_bitwise():
+    w = synth.make_workload([300, 2000, 65], s_q=2, h_q=32, causal=True, seed=23, extra_pages=5)
+    case(w, "page permutation")
+    o1, l1 = run_gpu(w)
+    rng = np.random.default_rng(5)
+    perm = rng.permutation(w.kcache.shape[0])
+    moved = np.empty_like(w.kcache)
+    moved[perm] = w.kcache
+    w.kcache = moved
+    w.block_table = perm[w.block_table].astype(np.int32)
+    o2, l2 = run_gpu(w)
+    np.testing.assert_array_equal(o1, o2)
+    np.testing.assert_array_equal(l1, l2)
+
+
+def test_poison_in_unread_memory():
+    lens = [65, 128, 3, 0, 191, 1000]
+    clean = synth.make_workload(lens, s_q=2, h_q=16, causal=True, seed=24, extra_pages=2,
+                                table_width=20)
+    dirty = synth.make_workload(lens, s_q=2, h_q=16, causal=True, seed=24, extra_pages=2,
+                                table_width=20, pad="poison", poison_tail=True)
+    case(dirty, "poison")
+    o1, l1 = run_gpu(clean)
+    o2, l2 = run_gpu(dirty)
+    assert np.isfinite(o2).all()
+    np.testing.assert_array_equal(o1, o2)
+    np.testing.assert_array_equal(l1, l2)
+    check_parity(o2, l2, *ref(dirty), what="poison")
+
+
+def test_two_kv_heads():
+    w = synth.make_workload([300, 1200], s_q=2, h_q=32, h_kv=2, causal=True, seed=25)
+    case(w, "h_kv=2")
+    out, lse = run_gpu(w)
+    check_parity(out, lse, *ref(w), what="h_kv=2")
+
+
+def test_constant_value_rows():
+    w = synth.make_workload([500, 37], s_q=1, h_q=16, seed=26)
+    c = synth.bf16_bits(np.array([-1.375], dtype=np.float32))[0]
+    w.kcache[..., :512] = c
+    case(w, "constant V")
+    out, lse = run_gpu(w)
+    np.testing.assert_array_equal(out, -1.375)
+    check_parity(out, lse, *ref(w), what="constant V")
+
+
+@pytest.mark.parametrize("name,seqs", [("membound", [0, 13, 31]), ("mtp", [0, 17, 63]),
+                                       ("large", [0, 64, 127]), ("ragged", [0, 3, 8, 11])])
+def test_full_size_sampled(name, seqs):
+    """Full-size workload in the benchmark's launch configuration; the oracle
+    recomputes whole sequences of it (the same pages and queries)."""
+    w = synth.named_workload(name)
+    case(w, f"full {name}")
+    out, lse = run_gpu(w)
+    sub = subset(w, seqs)
+    rout, rlse = ref(sub)
+    check_parity(out[seqs], lse[seqs], rout, rlse, what=f"{name} seqs {seqs}")
+    assert np.isfinite(out).all()
+    assert np.isfinite(lse).all()

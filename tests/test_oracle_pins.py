@@ -331,33 +331,32 @@ def test_bad_page_index_is_rejected():
 # Scheduler: brute-force enumeration and exact cover
 # --------------------------------------------------------------------------
 
-def enumerate_parts(seqlens, num_parts, fixed_cost):
-    """Part of every page, page by page, straight from the cost-interval rule."""
-    pages = [(int(n) + PAGE - 1) // PAGE for n in seqlens]
-    total = sum(p + fixed_cost for p in pages)
+def enumerate_parts(seqlens, num_parts, fixed_cost, unit):
+    """Part of every unit, unit by unit, straight from the cost-interval rule."""
+    units = [(int(n) + unit - 1) // unit for n in seqlens]
+    total = sum(u + fixed_cost for u in units)
     T = max(1, -(-total // num_parts))
     cost = 0
     where = []
-    for p in pages:
+    for u in units:
         cost += fixed_cost
-        if p == 0:
+        if u == 0:
             where.append([(cost - 1) // T])
         else:
-            where.append([(cost + i) // T for i in range(p)])
-        cost += p
-    return pages, where, T
+            where.append([(cost + i) // T for i in range(u)])
+        cost += u
+    return units, where, T
 
 
-def pieces_from_meta(meta, num_splits, seqlens):
-    """Expand tile metadata into {(b, split): (part, page_lo, page_hi)}."""
-    pages = [(int(n) + PAGE - 1) // PAGE for n in seqlens]
+def pieces_from_meta(meta, seqlens):
+    """Expand tile metadata into {(b, split): (part, key_lo, key_hi)}."""
     got = {}
     for p, w in enumerate(meta):
-        bb, pb, be, pe, k0 = (int(x) for x in w[:5])
+        bb, kb, be, ke, k0 = (int(x) for x in w[:5])
         assert (w[5:] == 0).all()
         for b in range(bb, be + 1):
-            lo = pb if b == bb else 0
-            hi = pe if b == be else pages[b]
+            lo = kb if b == bb else 0
+            hi = ke if b == be else int(seqlens[b])
             k = k0 if b == bb else 0
             assert (b, k) not in got
             got[(b, k)] = (p, lo, hi)
@@ -365,7 +364,7 @@ def pieces_from_meta(meta, num_splits, seqlens):
 
 
 @pytest.mark.parametrize("seed", range(40))
-def test_schedule_matches_page_enumeration(seed):
+def test_schedule_matches_unit_enumeration(seed):
     rng = np.random.default_rng(seed)
     B = int(rng.integers(1, 40))
     lens = rng.integers(0, 3000, size=B)
@@ -373,9 +372,10 @@ def test_schedule_matches_page_enumeration(seed):
         lens[rng.integers(0, B)] = 0
     num_parts = int(rng.integers(1, 300))
     fixed_cost = int(rng.integers(1, 6))
-    meta, ns = oracle.schedule(lens, num_parts=num_parts, fixed_cost=fixed_cost)
-    pages, where, T = enumerate_parts(lens, num_parts, fixed_cost)
-    got = pieces_from_meta(meta, ns, lens)
+    unit = int(rng.choice([16, 32, 64]))
+    meta, ns = oracle.schedule(lens, num_parts=num_parts, fixed_cost=fixed_cost, unit_tokens=unit)
+    units, where, T = enumerate_parts(lens, num_parts, fixed_cost, unit)
+    got = pieces_from_meta(meta, lens)
     assert ns[0] == 0
     for b in range(B):
         parts = sorted(set(where[b]))
@@ -385,14 +385,15 @@ def test_schedule_matches_page_enumeration(seed):
         for k, part in enumerate(parts):
             p, lo, hi = got[(b, k)]
             assert p == part
+            assert lo % unit == 0 and (hi % unit == 0 or hi == lens[b])
             covered.extend(range(lo, hi))
-            assert all(where[b][i] == p for i in range(lo, hi))
-        assert covered == list(range(pages[b]))       # exact cover, in order
+            assert all(where[b][i // unit] == p for i in range(lo, hi))
+        assert covered == list(range(int(lens[b])))     # exact cover of the keys, in order
     assert len(got) == ns[-1]
-    # balance: no part holds more than T cost units of pages
+    # balance: no part holds more than T units of keys
     per_part = np.zeros(num_parts, dtype=np.int64)
     for (b, k), (p, lo, hi) in got.items():
-        per_part[p] += hi - lo
+        per_part[p] += -(-(hi - lo) // unit)
     assert per_part.max() <= T
 
 
