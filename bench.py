@@ -1,0 +1,271 @@
+#!/usr/bin/env python3
+"""Benchmark of the paged MLA decode hot path on one MI355X.
+
+One step = the whole path over one batch of synthetic input: the split-KV
+metadata call (mla_get_metadata), the main kernel (mla_decode_splitkv) and
+the split combine (mla_decode_combine), all on the current stream.
+
+Default workload ("membound"): B=32, s_q=1, h_q=16, h_kv=1, every N=4096,
+page 64, bf16 N(0,1) data, scale 576^-0.5.  Inputs are resident in HBM before
+the timed region; every step reads a different copy of the KV pool (copies
+rotate over >= 1 GiB) so that the 256 MB Infinity Cache cannot serve the
+pool from the previous step.
+
+Output: one JSON line on stdout (details on stderr).
+  value       algorithmic bytes per step / time per step (TB/s); bytes =
+              every visible KV row once + q + out + lse + needed table entries
+              + cache_seqlens (no padding, re-reads or split partials)
+  roofline    the main decode kernel alone: algorithmic bytes per launch /
+              its mean duration from HIP events recorded around each launch
+              on the launch stream, against 8 TB/s (or its flops against
+              2.5 PFLOP/s bf16 for MFMA-bound workloads); traffic = HBM bytes
+              per launch from the committed rocprofv3 counter summary when it
+              matches the current kernel source, else null
+  cpu_baseline  the CPU oracle (fp64, OpenMP) on the same workload
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
+COUNTERS = os.path.join(ROOT, "profiles", "decode_kernel_counters.json")
+METRIC = "paged MLA decode: achieved HBM TB/s (h_q=16) and TFLOPS (h_q=128)"
+
+
+def eprint(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def algorithmic_units(w):
+    """Bytes and flops the method must move / compute for one call."""
+    n = w.seqlens.astype(np.int64)
+    B = n.shape[0]
+    pages = int(((n + 63) // 64).sum())
+    rows = B * w.s_q * w.h_q
+    nbytes = int(n.sum()) * w.h_kv * 576 * 2 + rows * (576 * 2 + 512 * 2 + 4) + pages * 4 + B * 4
+    pairs = 0
+    for t in range(w.s_q):
+        vis = np.minimum(n, n - w.s_q + t + 1) if w.causal else n
+        pairs += int(np.clip(vis, 0, None).sum())
+    flops = 2 * (576 + 512) * pairs * w.h_q
+    return nbytes, flops
+
+
+def kernel_source_digest():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "mla_decode_attention_split_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".hip", ".hpp")):
+            with open(os.path.join(csrc, name), "rb") as f:
+                h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def counter_traffic(workload):
+    """HBM bytes per launch of the decode kernel from the committed counter
+    summary, if it was taken on this workload with the current source."""
+    try:
+        with open(COUNTERS) as f:
+            c = json.load(f)
+    except (OSError, ValueError):
+        return None
+    entry = c.get("workloads", {}).get(workload)
+    if not entry or c.get("kernel_source_digest") != kernel_source_digest():
+        return None
+    return entry.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, min_seconds=10.0):
+    import oracle
+    oracle.build(force=False)
+    nbytes, flops = algorithmic_units(w)
+    times = []
+    t_end = time.perf_counter() + min_seconds
+    while time.perf_counter() < t_end or len(times) < 3:
+        t0 = time.perf_counter()
+        oracle.decode(w.q, w.kcache, w.block_table, w.seqlens, causal=w.causal, scale=w.scale)
+        times.append(time.perf_counter() - t0)
+    med = statistics.median(times)
+    return {"value": nbytes / med / 1e12, "unit": "TB/s", "cores": oracle.num_threads(),
+            "kind": "oracle", "tflops": flops / med / 1e12,
+            "sample": f"whole {w.name} workload ({w.batch} sequences), median of {len(times)} "
+                      f"runs of {med:.3f} s, fp64"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=500)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--workload", default="membound",
+                    choices=["tiny", "membound", "mtp", "large", "ragged"])
+    ap.add_argument("--rotate-bytes", type=float, default=float(1 << 30),
+                    help="total bytes of KV pool copies the steps rotate over")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy (to scale HBM counters)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE "
+              f"{world}); this path has no multi-GPU leg.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if not torch.cuda.is_available():
+        eprint("no GPU visible")
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    if args.copy_calibration:
+        n = 1 << 30
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        eprint(f"copied {n} bytes x 5")
+        return
+
+    import mla_decode_attention_split_amd as mla
+    from mla_decode_attention_split_amd import synth
+
+    w = synth.named_workload(args.workload)
+    nbytes, flops = algorithmic_units(w)
+    M, h_kv = w.rows_per_kv_head, w.h_kv
+    pool_bytes = w.kcache.nbytes
+    copies = max(1, int(np.ceil(args.rotate_bytes / pool_bytes)))
+    eprint(f"workload {w.name}: B={w.batch} s_q={w.s_q} h_q={w.h_q} h_kv={h_kv} "
+           f"causal={w.causal} sum(N)={int(w.seqlens.sum())} bytes={nbytes / 1e6:.2f} MB "
+           f"flops={flops / 1e9:.2f} GFLOP pool={pool_bytes / 1e6:.1f} MB x{copies} copies")
+
+    q = torch.from_numpy(w.q.view(np.int16)).to(dev).view(torch.bfloat16)
+    kv0 = torch.from_numpy(w.kcache.view(np.int16)).to(dev).view(torch.bfloat16)
+    kvs = [kv0] + [kv0.clone() for _ in range(copies - 1)]
+    bt = torch.from_numpy(np.ascontiguousarray(w.block_table)).to(dev)
+    sl = torch.from_numpy(np.ascontiguousarray(w.seqlens)).to(dev)
+    num_parts, fixed_cost, tile_rows = mla.mla_get_metadata_shape(w.batch, M, h_kv)
+    meta = torch.empty((num_parts, 8), dtype=torch.int32, device=dev)
+    splits = torch.empty((w.batch + 1,), dtype=torch.int32, device=dev)
+    out = torch.empty((w.batch, w.s_q, w.h_q, 512), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((w.batch, w.s_q, w.h_q), dtype=torch.float32, device=dev)
+    ws = torch.empty((mla.mla_decode_workspace_size(w.batch, M, h_kv, num_parts),),
+                     dtype=torch.uint8, device=dev)
+    eprint(f"num_parts={num_parts} fixed_cost={fixed_cost} tile_rows={tile_rows} "
+           f"grid={num_parts * ((M + tile_rows - 1) // tile_rows) * h_kv}")
+
+    def step(i, ev=None):
+        mla.mla_get_metadata(sl, M, h_kv, num_parts=num_parts, fixed_cost=fixed_cost,
+                             tile_metadata=meta, num_splits=splits)
+        if ev is not None:
+            ev[0].record()
+        mla.mla_decode_splitkv(q, kvs[i % copies], bt, sl, meta, splits, causal=w.causal,
+                               softmax_scale=w.scale, out=out, lse=lse, workspace=ws)
+        if ev is not None:
+            ev[1].record()
+        mla.mla_decode_combine(splits, out, lse, ws, num_parts=num_parts, h_kv=h_kv)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    # Host enqueue rate, to size the spin that holds the stream while the
+    # timed steps are queued (so the GPU then runs them back to back).
+    t0 = time.perf_counter()
+    for i in range(20):
+        step(i)
+    enqueue_s = (time.perf_counter() - t0) / 20
+    torch.cuda.synchronize()
+    hold_cycles = int(2.4e9 * (1.5 * enqueue_s * args.steps + 0.01))
+
+    # Pass 1: throughput of whole steps (events only at the ends).
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    torch.cuda._sleep(hold_cycles)
+    t0 = time.perf_counter()
+    e0.record()
+    for i in range(args.steps):
+        step(i)
+    e1.record()
+    t_enq = time.perf_counter() - t0
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = e0.elapsed_time(e1) / args.steps
+
+    # Pass 2: the main kernel alone, events around every launch.
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    torch.cuda._sleep(hold_cycles)
+    for i in range(args.steps):
+        step(i, evs[i])
+    torch.cuda.synchronize()
+    dec_ms = [a.elapsed_time(b) for a, b in evs]
+    dec_mean_ms = float(np.mean(dec_ms))
+
+    value_tbs = nbytes / (ms_per_step * 1e-3) / 1e12
+    hbm_bound = args.workload != "mtp"
+    if hbm_bound:
+        achieved = nbytes / (dec_mean_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4)}
+    else:
+        achieved = flops / (dec_mean_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4)}
+    traffic = counter_traffic(args.workload)
+    roof["traffic"] = traffic
+
+    eprint(f"host enqueue {enqueue_s * 1e6:.1f} us/step, timed loop enqueued in {t_enq * 1e3:.1f} ms "
+           f"behind a {hold_cycles / 2.4e6:.1f} ms hold")
+    eprint(f"step {ms_per_step * 1e3:.2f} us (wall incl. hold {wall / args.steps * 1e6:.2f} us)  "
+           f"-> {value_tbs:.3f} TB/s, {flops / (ms_per_step * 1e-3) / 1e12:.1f} TFLOP/s")
+    eprint(f"decode kernel {dec_mean_ms * 1e3:.2f} us mean (min {min(dec_ms) * 1e3:.2f}, "
+           f"max {max(dec_ms) * 1e3:.2f}) -> {achieved:.1f} {roof['unit']} "
+           f"({roof['frac'] * 100:.1f}% of peak)")
+
+    result = {
+        "metric": METRIC,
+        "value": round(value_tbs, 4) if hbm_bound else round(flops / (ms_per_step * 1e-3) / 1e12, 2),
+        "unit": "TB/s" if hbm_bound else "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "s_q": w.s_q, "h_q": w.h_q,
+                   "h_kv": h_kv, "seqlens_sum": int(w.seqlens.sum()), "page": 64, "d": 576,
+                   "dv": 512, "causal": bool(w.causal), "kv_pool_copies": copies,
+                   "num_parts": num_parts},
+        "tflops": round(flops / (ms_per_step * 1e-3) / 1e12, 3),
+        "decode_kernel_us": round(dec_mean_ms * 1e3, 3),
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        eprint("cpu baseline (oracle) ...")
+        result["cpu_baseline"] = cpu_baseline(w)
+        eprint(f"cpu baseline {result['cpu_baseline']}")
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

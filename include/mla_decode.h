@@ -149,6 +149,32 @@ int mla_decode(const void *q, const void *blocked_k, const int32_t *block_table,
                float softmax_scale, void *out, float *lse, void *workspace,
                size_t workspace_bytes, void *stream);
 
+/*
+ * The two halves of mla_decode, for callers that schedule or time them
+ * separately (same section 4 of the cnblogs page: blockwise attention, then
+ * the merge of partial outputs).  mla_decode == mla_decode_splitkv followed
+ * by mla_decode_combine on the same stream with the same workspace.
+ *
+ * mla_decode_splitkv: same arguments and checks as mla_decode; enqueues only
+ * the main kernel.  Sequences with one piece get their final out/lse; the
+ * others leave fp32 partials in the workspace.
+ *
+ * mla_decode_combine: merges the partials of sequences with several pieces
+ * into out/lse (a sequence with one piece is left untouched).  batch, s_q,
+ * h_q, h_kv, num_parts, num_splits, workspace and workspace_bytes must be the
+ * values given to the preceding mla_decode_splitkv.
+ */
+int mla_decode_splitkv(const void *q, const void *blocked_k, const int32_t *block_table,
+                       const int32_t *cache_seqlens, int batch, int s_q, int h_q, int h_kv,
+                       int d, int dv, int num_pages, int page_size, int max_blocks_per_seq,
+                       const int32_t *tile_metadata, int num_parts, const int32_t *num_splits,
+                       int causal, float softmax_scale, void *out, float *lse, void *workspace,
+                       size_t workspace_bytes, void *stream);
+
+int mla_decode_combine(const int32_t *num_splits, int batch, int s_q, int h_q, int h_kv,
+                       int num_parts, void *out, float *lse, const void *workspace,
+                       size_t workspace_bytes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

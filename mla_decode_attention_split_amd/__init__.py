@@ -20,7 +20,8 @@ import os
 
 __all__ = [
     "MlaError", "library_path", "mla_get_metadata_shape", "mla_get_metadata",
-    "mla_decode_workspace_size", "mla_decode", "get_mla_metadata", "flash_mla_with_kvcache",
+    "mla_decode_workspace_size", "mla_decode", "mla_decode_splitkv", "mla_decode_combine",
+    "get_mla_metadata", "flash_mla_with_kvcache",
     "HEAD_DIM", "VALUE_DIM", "PAGE_SIZE",
 ]
 
@@ -66,9 +67,14 @@ def _load():
     lib.mla_get_metadata.restype = i
     lib.mla_decode_workspace_size.argtypes = [i, i, i, i]
     lib.mla_decode_workspace_size.restype = sz
-    lib.mla_decode.argtypes = [p, p, p, p, i, i, i, i, i, i, i, i, i, p, i, p, i, ctypes.c_float,
-                               p, p, p, sz, p]
+    decode_args = [p, p, p, p, i, i, i, i, i, i, i, i, i, p, i, p, i, ctypes.c_float, p, p, p, sz,
+                   p]
+    lib.mla_decode.argtypes = decode_args
     lib.mla_decode.restype = i
+    lib.mla_decode_splitkv.argtypes = decode_args
+    lib.mla_decode_splitkv.restype = i
+    lib.mla_decode_combine.argtypes = [p, i, i, i, i, i, p, p, p, sz, p]
+    lib.mla_decode_combine.restype = i
     _lib = lib
     return lib
 
@@ -94,11 +100,13 @@ def mla_get_metadata_shape(batch: int, q_rows_per_kv_head: int, h_kv: int):
 
 
 def mla_get_metadata(cache_seqlens, q_rows_per_kv_head: int, h_kv: int, *,
-                     num_parts: int | None = None, fixed_cost: int | None = None):
+                     num_parts: int | None = None, fixed_cost: int | None = None,
+                     tile_metadata=None, num_splits=None):
     """Split-KV scheduling metadata on the device of ``cache_seqlens``.
 
     Returns ``(tile_metadata int32 [num_parts, 8], num_splits int32 [B+1])``;
     ``num_parts`` / ``fixed_cost`` default to :func:`mla_get_metadata_shape`.
+    Preallocated output tensors may be passed in.
     """
     import torch
     if cache_seqlens.dtype != torch.int32 or not cache_seqlens.is_cuda or cache_seqlens.dim() != 1:
@@ -106,11 +114,22 @@ def mla_get_metadata(cache_seqlens, q_rows_per_kv_head: int, h_kv: int, *,
     seqlens = cache_seqlens.contiguous()
     batch = seqlens.shape[0]
     with torch.cuda.device(seqlens.device):
-        dn, df, _ = mla_get_metadata_shape(batch, q_rows_per_kv_head, h_kv)
-        num_parts = dn if num_parts is None else int(num_parts)
-        fixed_cost = df if fixed_cost is None else int(fixed_cost)
-        meta = torch.empty((num_parts, METADATA_WORDS), dtype=torch.int32, device=seqlens.device)
-        splits = torch.empty((batch + 1,), dtype=torch.int32, device=seqlens.device)
+        if num_parts is None or fixed_cost is None:
+            dn, df, _ = mla_get_metadata_shape(batch, q_rows_per_kv_head, h_kv)
+            num_parts = dn if num_parts is None else int(num_parts)
+            fixed_cost = df if fixed_cost is None else int(fixed_cost)
+        meta = tile_metadata
+        if meta is None:
+            meta = torch.empty((num_parts, METADATA_WORDS), dtype=torch.int32,
+                               device=seqlens.device)
+        elif (meta.dtype != torch.int32 or tuple(meta.shape) != (num_parts, METADATA_WORDS)
+              or not meta.is_contiguous()):
+            raise ValueError("tile_metadata must be contiguous int32 [num_parts, 8]")
+        splits = num_splits
+        if splits is None:
+            splits = torch.empty((batch + 1,), dtype=torch.int32, device=seqlens.device)
+        elif splits.dtype != torch.int32 or tuple(splits.shape) != (batch + 1,):
+            raise ValueError("num_splits must be int32 [B+1]")
         _check(_load().mla_get_metadata(seqlens.data_ptr(), batch, int(q_rows_per_kv_head),
                                         int(h_kv), num_parts, fixed_cost, meta.data_ptr(),
                                         splits.data_ptr(), _stream_of(seqlens.device)))
@@ -123,13 +142,8 @@ def mla_decode_workspace_size(batch: int, q_rows_per_kv_head: int, h_kv: int,
                                                  int(num_parts)))
 
 
-def mla_decode(q, blocked_k, block_table, cache_seqlens, tile_metadata, num_splits, *,
-               causal: bool = False, softmax_scale: float | None = None, out=None, lse=None,
-               workspace=None):
-    """Paged MLA decode.  ``q`` bf16 [B, s_q, h_q, 576]; ``blocked_k`` bf16
-    [num_pages, 64, h_kv, 576]; ``block_table`` int32 [B, max_blocks];
-    ``cache_seqlens`` int32 [B].  Returns ``(out bf16 [B, s_q, h_q, 512],
-    lse fp32 [B, s_q, h_q])``."""
+def _decode_call(fn_name, q, blocked_k, block_table, cache_seqlens, tile_metadata, num_splits,
+                 causal, softmax_scale, out, lse, workspace):
     import torch
     if q.dtype != torch.bfloat16 or blocked_k.dtype != torch.bfloat16:
         raise ValueError("q and blocked_k must be bfloat16")
@@ -166,13 +180,51 @@ def mla_decode(q, blocked_k, block_table, cache_seqlens, tile_metadata, num_spli
         need = mla_decode_workspace_size(B, M, h_kv, num_parts) if h_q % max(h_kv, 1) == 0 else 0
         if workspace is None:
             workspace = torch.empty((max(need, 16),), dtype=torch.uint8, device=dev)
-        _check(_load().mla_decode(
-            q.data_ptr(), blocked_k.data_ptr(), block_table.data_ptr(), cache_seqlens.data_ptr(),
-            B, s_q, h_q, h_kv, d, VALUE_DIM, num_pages, page, block_table.shape[1],
-            tile_metadata.data_ptr(), num_parts, num_splits.data_ptr(), int(bool(causal)), scale,
-            out.data_ptr(), lse.data_ptr(), workspace.data_ptr(),
-            workspace.numel() * workspace.element_size(), _stream_of(dev)))
+        fn = getattr(_load(), fn_name)
+        _check(fn(q.data_ptr(), blocked_k.data_ptr(), block_table.data_ptr(),
+                  cache_seqlens.data_ptr(), B, s_q, h_q, h_kv, d, VALUE_DIM, num_pages, page,
+                  block_table.shape[1], tile_metadata.data_ptr(), num_parts, num_splits.data_ptr(),
+                  int(bool(causal)), scale, out.data_ptr(), lse.data_ptr(), workspace.data_ptr(),
+                  workspace.numel() * workspace.element_size(), _stream_of(dev)))
+    return out, lse, workspace
+
+
+def mla_decode(q, blocked_k, block_table, cache_seqlens, tile_metadata, num_splits, *,
+               causal: bool = False, softmax_scale: float | None = None, out=None, lse=None,
+               workspace=None):
+    """Paged MLA decode.  ``q`` bf16 [B, s_q, h_q, 576]; ``blocked_k`` bf16
+    [num_pages, 64, h_kv, 576]; ``block_table`` int32 [B, max_blocks];
+    ``cache_seqlens`` int32 [B].  Returns ``(out bf16 [B, s_q, h_q, 512],
+    lse fp32 [B, s_q, h_q])``."""
+    out, lse, _ = _decode_call("mla_decode", q, blocked_k, block_table, cache_seqlens,
+                               tile_metadata, num_splits, causal, softmax_scale, out, lse,
+                               workspace)
     return out, lse
+
+
+def mla_decode_splitkv(q, blocked_k, block_table, cache_seqlens, tile_metadata, num_splits, *,
+                       causal: bool = False, softmax_scale: float | None = None, out=None,
+                       lse=None, workspace=None):
+    """Main kernel only; returns ``(out, lse, workspace)`` -- pass the same
+    ``out``, ``lse`` and ``workspace`` to :func:`mla_decode_combine`."""
+    return _decode_call("mla_decode_splitkv", q, blocked_k, block_table, cache_seqlens,
+                        tile_metadata, num_splits, causal, softmax_scale, out, lse, workspace)
+
+
+def mla_decode_combine(num_splits, out, lse, workspace, *, num_parts: int, h_kv: int = 1):
+    """Merge the split partials left by :func:`mla_decode_splitkv`."""
+    B, s_q, h_q, _ = out.shape
+    with _torch_device(out.device):
+        _check(_load().mla_decode_combine(
+            num_splits.data_ptr(), B, s_q, h_q, int(h_kv), int(num_parts), out.data_ptr(),
+            lse.data_ptr(), workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+            _stream_of(out.device)))
+    return out, lse
+
+
+def _torch_device(dev):
+    import torch
+    return torch.cuda.device(dev)
 
 
 def get_mla_metadata(cache_seqlens, num_heads_per_head_k: int, num_heads_k: int):

@@ -93,9 +93,10 @@ int mla_get_metadata_shape(int batch, int q_rows_per_kv_head, int h_kv, int* num
   int parts = cus / (m_tiles * h_kv);
   parts = parts >= 8 ? (parts / 8) * 8 : 8;
   if (num_parts) *num_parts = parts;
-  // Per-sequence overhead in 32-key units: query load, epilogue and the
-  // combine of one more piece.
-  if (fixed_cost) *fixed_cost = 2 + tr / 64;
+  // Per-sequence overhead in 32-key stage units: the query stages of a piece
+  // (one per 32 query rows of the tile) plus about one stage for the
+  // epilogue and the merge of one more piece.
+  if (fixed_cost) *fixed_cost = (tr + 31) / 32 + 1;
   if (tile_rows) *tile_rows = tr;
   return ok();
 }
@@ -131,12 +132,15 @@ size_t mla_decode_workspace_size(int batch, int q_rows_per_kv_head, int h_kv, in
   return o_bytes + l_bytes;
 }
 
-int mla_decode(const void* q, const void* blocked_k, const int32_t* block_table,
-               const int32_t* cache_seqlens, int batch, int s_q, int h_q, int h_kv, int d, int dv,
-               int num_pages, int page_size, int max_blocks_per_seq,
-               const int32_t* tile_metadata, int num_parts, const int32_t* num_splits, int causal,
-               float softmax_scale, void* out, float* lse, void* workspace,
-               size_t workspace_bytes, void* stream) {
+namespace {
+
+// Shared checks and argument packing of mla_decode / mla_decode_splitkv.
+int prepare_decode(const void* q, const void* blocked_k, const int32_t* block_table,
+                   const int32_t* cache_seqlens, int batch, int s_q, int h_q, int h_kv, int d,
+                   int dv, int num_pages, int page_size, int max_blocks_per_seq,
+                   const int32_t* tile_metadata, int num_parts, const int32_t* num_splits,
+                   int causal, float softmax_scale, void* out, float* lse, void* workspace,
+                   size_t workspace_bytes, mla::DecodeArgs* a, int* tile_rows) {
   if (d != MLA_HEAD_DIM) return fail(MLA_ERR_UNSUPPORTED, "head dim %d (only %d)", d, MLA_HEAD_DIM);
   if (dv != MLA_VALUE_DIM)
     return fail(MLA_ERR_UNSUPPORTED, "value dim %d (only %d)", dv, MLA_VALUE_DIM);
@@ -172,50 +176,128 @@ int mla_decode(const void* q, const void* blocked_k, const int32_t* block_table,
   const int tr = mla::tile_rows_for(M);
   const size_t pieces = (size_t)batch + (size_t)num_parts;
   const size_t rows = pieces * (size_t)h_kv * (size_t)M;
+  a->q = static_cast<const uint16_t*>(q);
+  a->kv = static_cast<const uint16_t*>(blocked_k);
+  a->block_table = block_table;
+  a->seqlens = cache_seqlens;
+  a->meta = tile_metadata;
+  a->num_splits = num_splits;
+  a->out = static_cast<uint16_t*>(out);
+  a->lse = lse;
+  a->o_part = static_cast<float*>(workspace);
+  a->lse_part = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                         rows * MLA_VALUE_DIM * sizeof(float));
+  a->batch = batch;
+  a->s_q = s_q;
+  a->h_q = h_q;
+  a->h_kv = h_kv;
+  a->M = M;
+  a->max_blocks = max_blocks_per_seq;
+  a->num_parts = num_parts;
+  a->m_tiles = (M + tr - 1) / tr;
+  a->causal = causal ? 1 : 0;
+  a->xcd_map = (num_parts % 8 == 0) ? 1 : 0;
+  a->scale_log2 = softmax_scale * 1.44269504088896340736f;
+  const long long grid = (long long)num_parts * a->m_tiles * h_kv;
+  if (grid > 0x7fffffffLL) return fail(MLA_ERR_UNSUPPORTED, "grid too large");
+  *tile_rows = tr;
+  return MLA_OK;
+}
 
+int enqueue_combine(const mla::DecodeArgs& a, hipStream_t st) {
+  mla::CombineArgs c;
+  c.num_splits = a.num_splits;
+  c.o_part = a.o_part;
+  c.lse_part = a.lse_part;
+  c.out = a.out;
+  c.lse = a.lse;
+  c.batch = a.batch;
+  c.s_q = a.s_q;
+  c.h_q = a.h_q;
+  c.h_kv = a.h_kv;
+  c.M = a.M;
+  hipError_t e = mla::launch_combine(c, st);
+  if (e != hipSuccess) return fail(MLA_ERR_HIP, "combine launch: %s", hipGetErrorString(e));
+  return MLA_OK;
+}
+
+}  // namespace
+
+int mla_decode_splitkv(const void* q, const void* blocked_k, const int32_t* block_table,
+                       const int32_t* cache_seqlens, int batch, int s_q, int h_q, int h_kv,
+                       int d, int dv, int num_pages, int page_size, int max_blocks_per_seq,
+                       const int32_t* tile_metadata, int num_parts, const int32_t* num_splits,
+                       int causal, float softmax_scale, void* out, float* lse, void* workspace,
+                       size_t workspace_bytes, void* stream) {
   mla::DecodeArgs a;
-  a.q = static_cast<const uint16_t*>(q);
-  a.kv = static_cast<const uint16_t*>(blocked_k);
-  a.block_table = block_table;
-  a.seqlens = cache_seqlens;
-  a.meta = tile_metadata;
+  int tr = 0;
+  int rc = prepare_decode(q, blocked_k, block_table, cache_seqlens, batch, s_q, h_q, h_kv, d, dv,
+                          num_pages, page_size, max_blocks_per_seq, tile_metadata, num_parts,
+                          num_splits, causal, softmax_scale, out, lse, workspace,
+                          workspace_bytes, &a, &tr);
+  if (rc != MLA_OK) return rc;
+  hipError_t e = mla::launch_decode(a, tr, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(MLA_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+int mla_decode_combine(const int32_t* num_splits, int batch, int s_q, int h_q, int h_kv,
+                       int num_parts, void* out, float* lse, const void* workspace,
+                       size_t workspace_bytes, void* stream) {
+  if (batch < 1 || batch > MLA_MAX_BATCH)
+    return fail(MLA_ERR_INVALID_ARG, "batch %d outside [1, %d]", batch, MLA_MAX_BATCH);
+  if (s_q < 1 || h_q < 1 || h_kv < 1 || h_q % h_kv != 0)
+    return fail(MLA_ERR_INVALID_ARG, "s_q %d, h_q %d, h_kv %d (need h_q %% h_kv == 0)", s_q, h_q,
+                h_kv);
+  const long long M_ll = (long long)s_q * (h_q / h_kv);
+  if (M_ll > MLA_MAX_ROWS)
+    return fail(MLA_ERR_UNSUPPORTED, "s_q * h_q / h_kv = %lld > %d", M_ll, MLA_MAX_ROWS);
+  if (num_parts < 1 || num_parts > MLA_MAX_PARTS)
+    return fail(MLA_ERR_INVALID_ARG, "num_parts %d outside [1, %d]", num_parts, MLA_MAX_PARTS);
+  if (!num_splits || !out || !lse || !workspace)
+    return fail(MLA_ERR_INVALID_ARG, "null pointer argument");
+  if (!aligned16(out) || !aligned16(workspace))
+    return fail(MLA_ERR_INVALID_ARG, "out and workspace must be 16-byte aligned");
+  const int M = (int)M_ll;
+  const size_t need = mla_decode_workspace_size(batch, M, h_kv, num_parts);
+  if (workspace_bytes < need)
+    return fail(MLA_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", workspace_bytes, need);
+  const size_t rows = ((size_t)batch + (size_t)num_parts) * (size_t)h_kv * (size_t)M;
+  mla::DecodeArgs a{};
   a.num_splits = num_splits;
+  a.o_part = const_cast<float*>(static_cast<const float*>(workspace));
+  a.lse_part = reinterpret_cast<float*>(const_cast<char*>(static_cast<const char*>(workspace)) +
+                                        rows * MLA_VALUE_DIM * sizeof(float));
   a.out = static_cast<uint16_t*>(out);
   a.lse = lse;
-  a.o_part = static_cast<float*>(workspace);
-  a.lse_part = reinterpret_cast<float*>(static_cast<char*>(workspace) +
-                                        rows * MLA_VALUE_DIM * sizeof(float));
   a.batch = batch;
   a.s_q = s_q;
   a.h_q = h_q;
   a.h_kv = h_kv;
   a.M = M;
-  a.max_blocks = max_blocks_per_seq;
-  a.num_parts = num_parts;
-  a.m_tiles = (M + tr - 1) / tr;
-  a.causal = causal ? 1 : 0;
-  a.xcd_map = (num_parts % 8 == 0) ? 1 : 0;
-  a.scale_log2 = softmax_scale * 1.44269504088896340736f;
-  const long long grid = (long long)num_parts * a.m_tiles * h_kv;
-  if (grid > 0x7fffffffLL) return fail(MLA_ERR_UNSUPPORTED, "grid too large");
+  int rc = enqueue_combine(a, static_cast<hipStream_t>(stream));
+  if (rc != MLA_OK) return rc;
+  return ok();
+}
 
+int mla_decode(const void* q, const void* blocked_k, const int32_t* block_table,
+               const int32_t* cache_seqlens, int batch, int s_q, int h_q, int h_kv, int d, int dv,
+               int num_pages, int page_size, int max_blocks_per_seq,
+               const int32_t* tile_metadata, int num_parts, const int32_t* num_splits, int causal,
+               float softmax_scale, void* out, float* lse, void* workspace,
+               size_t workspace_bytes, void* stream) {
+  mla::DecodeArgs a;
+  int tr = 0;
+  int rc = prepare_decode(q, blocked_k, block_table, cache_seqlens, batch, s_q, h_q, h_kv, d, dv,
+                          num_pages, page_size, max_blocks_per_seq, tile_metadata, num_parts,
+                          num_splits, causal, softmax_scale, out, lse, workspace,
+                          workspace_bytes, &a, &tr);
+  if (rc != MLA_OK) return rc;
   hipStream_t st = static_cast<hipStream_t>(stream);
   hipError_t e = mla::launch_decode(a, tr, st);
   if (e != hipSuccess) return fail(MLA_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
-
-  mla::CombineArgs c;
-  c.num_splits = num_splits;
-  c.o_part = a.o_part;
-  c.lse_part = a.lse_part;
-  c.out = a.out;
-  c.lse = lse;
-  c.batch = batch;
-  c.s_q = s_q;
-  c.h_q = h_q;
-  c.h_kv = h_kv;
-  c.M = M;
-  e = mla::launch_combine(c, st);
-  if (e != hipSuccess) return fail(MLA_ERR_HIP, "combine launch: %s", hipGetErrorString(e));
+  rc = enqueue_combine(a, st);
+  if (rc != MLA_OK) return rc;
   return ok();
 }
 

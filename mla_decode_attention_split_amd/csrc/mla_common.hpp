@@ -34,14 +34,27 @@ typedef int i32x4 __attribute__((ext_vector_type(4)));
 #define MLA_LDS __attribute__((address_space(3)))
 
 // XOR swizzle of the 16-byte chunk index inside each 128-byte group of a
-// cached row held in LDS.  Eight consecutive rows get eight distinct values
-// (conflict-free 16 B reads of one chunk across rows), and four consecutive
-// rows starting at a multiple of 4 map an aligned chunk pair to four
-// disjoint pairs (conflict-free transposed 8 B reads).
-__device__ __forceinline__ int swz(int row) { return 2 * (row & 3) + ((row >> 2) & 1); }
+// cached row held in LDS (rows are 1152 B; LDS has 64 banks of 4 B).  The
+// swizzle depends on the MFMA tile shape of the kernel that reads the stage;
+// each choice makes that kernel's two access patterns conflict-free (checked
+// with the bank-conflict counter):
+//   R = 16 (16x16x32 tiles): f(r) = r & 7
+//     16-byte K reads of 16 rows x one chunk, and transposed 8-byte V reads of
+//     8 rows x one aligned chunk pair;
+//   R = 32 (32x32x16 tiles): f(r) = bitrev3((r >> 1) & 7)
+//     16-byte K reads of 16 rows x one chunk, and transposed 8-byte V reads of
+//     4 rows x one aligned chunk quad.
+__device__ __forceinline__ int bitrev3(int x) { return ((x & 1) << 2) | (x & 2) | ((x >> 2) & 1); }
 
+template <int R>
+__device__ __forceinline__ int swz(int row) {
+  if constexpr (R == 16) return row & 7;
+  else return bitrev3((row >> 1) & 7);
+}
+
+template <int R>
 __device__ __forceinline__ int phys_chunk(int row, int chunk) {
-  return (chunk & ~7) | ((chunk & 7) ^ swz(row));
+  return (chunk & ~7) | ((chunk & 7) ^ swz<R>(row));
 }
 
 typedef float f32x2 __attribute__((ext_vector_type(2)));
@@ -55,6 +68,15 @@ __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
 // The two floats a packed bf16 pair stands for.
 __device__ __forceinline__ float bf16_lo(uint32_t p) { return __uint_as_float(p << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t p) { return __uint_as_float(p & 0xffff0000u); }
+
+// Uniform read of read-only metadata through the scalar cache, waited on in
+// the same asm block.  Used inside the stage loop, where the compiler would
+// otherwise emit a vector load whose wait drains the staged key loads.
+__device__ __forceinline__ int sload_i32(const int32_t* p) {
+  int v;
+  asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(p) : "memory");
+  return v;
+}
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
