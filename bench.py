@@ -16,12 +16,22 @@ Output: one JSON line on stdout (details on stderr).
               every visible KV row once + q + out + lse + needed table entries
               + cache_seqlens (no padding, re-reads or split partials)
   roofline    the main decode kernel alone: algorithmic bytes per launch /
-              its mean duration from HIP events recorded around each launch
-              on the launch stream, against 8 TB/s (or its flops against
+              its mean duration (HIP events on the launch stream around K
+              back-to-back launches), against 8 TB/s (or its flops against
               2.5 PFLOP/s bf16 for MFMA-bound workloads); traffic = HBM bytes
               per launch from the committed rocprofv3 counter summary when it
               matches the current kernel source, else null
   cpu_baseline  the CPU oracle (fp64, OpenMP) on the same workload
+
+Profile summaries: `--summarize-profiles DIR` turns the rocprofv3 output that
+the commands below leave in DIR into the text summaries and the counter file
+under profiles/ (run from /tmp, TMPDIR=/tmp; WL = membound or mtp):
+  rocprofv3 --kernel-trace --stats -d DIR/trace_WL -o run --output-format csv
+      -- python3 /root/repo/bench.py --workload WL --steps 100 --warmup 10 --no-cpu-baseline
+  rocprofv3 --pmc FETCH_SIZE -d DIR/pmc_FETCH_SIZE_WL -o run --output-format csv
+      -- python3 /root/repo/bench.py --workload WL --steps 5 --warmup 2 --no-cpu-baseline
+  (the same with WRITE_SIZE), and both counters once more with
+      -- python3 /root/repo/bench.py --copy-calibration   (dirs pmc_FETCH_SIZE_copy, ...)
 """
 from __future__ import annotations
 
@@ -105,6 +115,90 @@ def cpu_baseline(w, min_seconds=10.0):
                       f"runs of {med:.3f} s, fp64"}
 
 
+def _csv_rows(path):
+    import csv
+    with open(path) as f:
+        return list(csv.DictReader(f))
+
+
+def _per_kernel_counter(path):
+    """Mean counter value (KiB) per dispatch, per kernel name."""
+    acc = {}
+    for r in _csv_rows(path):
+        acc.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+    return {k: (sum(v) / len(v), len(v)) for k, v in acc.items()}
+
+
+def _short_kernel(name):
+    if "spin_kernel" in name:
+        return "torch spin_kernel (stream hold before timed passes)"
+    return name.split("(unsigned")[0].split("(int")[0].split("(mla::")[0].replace("void ", "")
+
+
+def summarize_profiles(d):
+    """Write profiles/<kernel>_<workload>.txt and profiles/decode_kernel_counters.json."""
+    out_dir = os.path.join(ROOT, "profiles")
+    os.makedirs(out_dir, exist_ok=True)
+    # Calibration: a plain 1 GiB device copy reads and writes 1 GiB.
+    copy_bytes = float(1 << 30) * 5
+    cal = {}
+    for c in ("FETCH_SIZE", "WRITE_SIZE"):
+        k = _per_kernel_counter(os.path.join(d, f"pmc_{c}_copy", "run_counter_collection.csv"))
+        copy = [(v, n) for name, (v, n) in k.items() if "copyBuffer" in name]
+        tot = sum(v * n for v, n in copy) * 1024.0
+        cal[c] = {"measured_bytes": tot, "true_bytes": copy_bytes, "scale": copy_bytes / tot}
+    counters = {"kernel_source_digest": kernel_source_digest(),
+                "calibration": {"kernel": "__amd_rocclr_copyBuffer (torch copy_ of 1 GiB, x5)",
+                                "fetch_scale": round(cal["FETCH_SIZE"]["scale"], 4),
+                                "write_scale": round(cal["WRITE_SIZE"]["scale"], 4)},
+                "workloads": {}}
+    for wl in ("membound", "mtp", "large", "ragged"):
+        tdir = os.path.join(d, f"trace_{wl}")
+        if not os.path.isdir(tdir):
+            continue
+        stats = _csv_rows(os.path.join(tdir, "run_kernel_stats.csv"))
+        fetch = _per_kernel_counter(os.path.join(d, f"pmc_FETCH_SIZE_{wl}", "run_counter_collection.csv"))
+        write = _per_kernel_counter(os.path.join(d, f"pmc_WRITE_SIZE_{wl}", "run_counter_collection.csv"))
+        import re
+        bench_err = [x for x in open(os.path.join(d, f"trace_{wl}.err")).read().strip().splitlines()
+                     if not re.match(r"^[WEI]\d{8} ", x)]
+        lines = [f"# rocprofv3 kernel trace: paged MLA decode, workload {wl}", "",
+                 "command (from /tmp, TMPDIR=/tmp):",
+                 f"  rocprofv3 --kernel-trace --stats -d DIR/trace_{wl} -o run --output-format csv "
+                 f"-- python3 /root/repo/bench.py --workload {wl} --steps 100 --warmup 10 --no-cpu-baseline",
+                 f"kernel source digest: {counters['kernel_source_digest']}", "",
+                 f"{'kernel':60s} {'calls':>6s} {'avg us':>9s} {'min us':>9s} {'max us':>9s}"]
+        for r in stats:
+            name = _short_kernel(r["Name"])
+            lines.append(f"{name[:60]:60s} {int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:9.2f} "
+                         f"{float(r['MinNs']) / 1e3:9.2f} {float(r['MaxNs']) / 1e3:9.2f}")
+        lines += ["", "bench.py stderr under the profiler:"] + ["  " + x for x in bench_err]
+        lines += ["", "HBM counters (separate runs, --steps 5 --warmup 2; KiB per dispatch, raw):"]
+        entry = None
+        for name, (fv, n) in fetch.items():
+            wv = write.get(name, (float("nan"), 0))[0]
+            short = _short_kernel(name)
+            lines.append(f"  {short[:58]:58s} FETCH_SIZE {fv:12.1f}  WRITE_SIZE {wv:12.1f}  ({n} dispatches)")
+            if "decode_kernel" in name:
+                fb = fv * 1024 * cal["FETCH_SIZE"]["scale"]
+                wb = wv * 1024 * cal["WRITE_SIZE"]["scale"]
+                entry = {"kernel": short, "fetch_kib_raw": round(fv, 1), "write_kib_raw": round(wv, 1),
+                         "hbm_read_bytes_per_launch": int(fb), "hbm_write_bytes_per_launch": int(wb),
+                         "hbm_bytes_per_launch": int(fb + wb)}
+        if entry:
+            counters["workloads"][wl] = entry
+            lines += ["", f"copy calibration: FETCH_SIZE x{cal['FETCH_SIZE']['scale']:.4f}, "
+                          f"WRITE_SIZE x{cal['WRITE_SIZE']['scale']:.4f} (1 GiB torch copy read/written 5 times)",
+                      f"decode kernel HBM bytes per launch: read {entry['hbm_read_bytes_per_launch'] / 1e6:.2f} MB, "
+                      f"write {entry['hbm_write_bytes_per_launch'] / 1e6:.2f} MB"]
+        with open(os.path.join(out_dir, f"decode_kernel_{wl}.txt"), "w") as f:
+            f.write("\n".join(lines) + "\n")
+    with open(COUNTERS, "w") as f:
+        json.dump(counters, f, indent=1)
+        f.write("\n")
+    print(json.dumps(counters, indent=1))
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -117,7 +211,12 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (to scale HBM counters)")
+    ap.add_argument("--summarize-profiles", metavar="DIR",
+                    help="write profiles/ summaries from rocprofv3 output in DIR and exit")
     args = ap.parse_args()
+    if args.summarize_profiles:
+        summarize_profiles(args.summarize_profiles)
+        return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -169,15 +268,11 @@ def main():
     eprint(f"num_parts={num_parts} fixed_cost={fixed_cost} tile_rows={tile_rows} "
            f"grid={num_parts * ((M + tile_rows - 1) // tile_rows) * h_kv}")
 
-    def step(i, ev=None):
+    def step(i):
         mla.mla_get_metadata(sl, M, h_kv, num_parts=num_parts, fixed_cost=fixed_cost,
                              tile_metadata=meta, num_splits=splits)
-        if ev is not None:
-            ev[0].record()
         mla.mla_decode_splitkv(q, kvs[i % copies], bt, sl, meta, splits, causal=w.causal,
                                softmax_scale=w.scale, out=out, lse=lse, workspace=ws)
-        if ev is not None:
-            ev[1].record()
         mla.mla_decode_combine(splits, out, lse, ws, num_parts=num_parts, h_kv=h_kv)
 
     for i in range(args.warmup):
@@ -207,16 +302,21 @@ def main():
     wall = time.perf_counter() - t0
     ms_per_step = e0.elapsed_time(e1) / args.steps
 
-    # Pass 2: the main kernel alone, events around every launch.
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
+    # Pass 2: the main kernel alone, launched back to back over the same
+    # metadata (computed once, outside the timed region), HIP events at both
+    # ends on the stream the kernel runs on; mean launch duration = span / K.
+    step(0)
     torch.cuda.synchronize()
+    d0 = torch.cuda.Event(enable_timing=True)
+    d1 = torch.cuda.Event(enable_timing=True)
     torch.cuda._sleep(hold_cycles)
+    d0.record()
     for i in range(args.steps):
-        step(i, evs[i])
+        mla.mla_decode_splitkv(q, kvs[i % copies], bt, sl, meta, splits, causal=w.causal,
+                               softmax_scale=w.scale, out=out, lse=lse, workspace=ws)
+    d1.record()
     torch.cuda.synchronize()
-    dec_ms = [a.elapsed_time(b) for a, b in evs]
-    dec_mean_ms = float(np.mean(dec_ms))
+    dec_mean_ms = d0.elapsed_time(d1) / args.steps
 
     value_tbs = nbytes / (ms_per_step * 1e-3) / 1e12
     hbm_bound = args.workload != "mtp"
@@ -235,8 +335,8 @@ def main():
            f"behind a {hold_cycles / 2.4e6:.1f} ms hold")
     eprint(f"step {ms_per_step * 1e3:.2f} us (wall incl. hold {wall / args.steps * 1e6:.2f} us)  "
            f"-> {value_tbs:.3f} TB/s, {flops / (ms_per_step * 1e-3) / 1e12:.1f} TFLOP/s")
-    eprint(f"decode kernel {dec_mean_ms * 1e3:.2f} us mean (min {min(dec_ms) * 1e3:.2f}, "
-           f"max {max(dec_ms) * 1e3:.2f}) -> {achieved:.1f} {roof['unit']} "
+    eprint(f"decode kernel {dec_mean_ms * 1e3:.2f} us mean over {args.steps} back-to-back launches "
+           f"-> {achieved:.1f} {roof['unit']} "
            f"({roof['frac'] * 100:.1f}% of peak)")
 
     result = {
