@@ -6,8 +6,11 @@
 // empty the row gets out = 0 and lse = -inf.  Sequences with a single piece
 // were written directly by the main kernel and are skipped here.
 //
-// One wave per query row: 64 lanes x 8 value dims, 16-byte loads of the
-// partials and one 16-byte bf16 store per lane.
+// One wave per query row.  The kernel is latency-bound at small batch, so
+// each wave makes three dependent trips to memory and no more: the split
+// range (scalar loads), the piece LSEs (lane k holds piece k, reduced across
+// the wave), then the partial rows, kUnroll pieces per trip (64 lanes x 8
+// value dims, two 16-byte loads per lane and piece).
 #include "mla_common.hpp"
 #include "mla_internal.hpp"
 
@@ -15,41 +18,79 @@ namespace mla {
 
 constexpr float kLog2e = 1.44269504088896340736f;
 constexpr float kLn2c = 0.69314718055994530942f;
+constexpr int kCombineRows = 4;  // waves (query rows) per workgroup
+constexpr int kUnroll = 8;       // pieces loaded per trip
 
-__global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) x = fmaxf(x, __shfl_xor(x, off, 64));
+  return x;
+}
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off, 64);
+  return x;
+}
+
+__global__ __launch_bounds__(64 * kCombineRows) void combine_kernel(CombineArgs a) {
   const int b = blockIdx.z;
   const int g = blockIdx.y;
-  const int m = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int s0 = sload_i32(a.num_splits + b);
+  const int nsplit = sload_i32(a.num_splits + b + 1) - s0;
+  const int m = blockIdx.x * kCombineRows + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
-  const int s0 = a.num_splits[b];
-  const int nsplit = a.num_splits[b + 1] - s0;
   if (nsplit <= 1 || m >= a.M) return;
 
   const long long stride = (long long)a.h_kv * a.M;  // rows between consecutive pieces
   const long long r0 = ((long long)s0 * a.h_kv + g) * a.M + m;
-  float mx = -INFINITY;
-  for (int k = 0; k < nsplit; ++k) mx = fmaxf(mx, a.lse_part[r0 + k * stride]);
+  const float* lse_row = a.lse_part + r0;
 
+  // L over all pieces, 64 at a time (lane k holds piece c + k); the first 64
+  // are loaded once and kept.
+  auto lse_at = [&](int c) -> float {
+    return c + lane < nsplit ? lse_row[(c + lane) * stride] : -INFINITY;
+  };
+  const float v0 = lse_at(0);
+  float mx = v0;
+  for (int c = 64; c < nsplit; c += 64) mx = fmaxf(mx, lse_at(c));
+  mx = wave_max(mx);
+  float L = -INFINITY;
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  if (mx > -INFINITY) {
+    float sum = 0.f;
+    for (int c = 0; c < nsplit; c += 64) sum += fast_exp2(((c == 0 ? v0 : lse_at(c)) - mx) * kLog2e);
+    L = mx + fast_log2(wave_sum(sum)) * kLn2c;
+    const float* o_row = a.o_part + r0 * kValueDim + lane * 8;
+    for (int c = 0; c < nsplit; c += 64) {
+      const float wl = fast_exp2(((c == 0 ? v0 : lse_at(c)) - L) * kLog2e);  // weight of piece c + lane
+      const int n = nsplit - c < 64 ? nsplit - c : 64;
+      for (int k0 = 0; k0 < n; k0 += kUnroll) {
+        float4 x[kUnroll][2];
+#pragma unroll
+        for (int j = 0; j < kUnroll; ++j) {
+          if (k0 + j < n) {
+            const float4* src = reinterpret_cast<const float4*>(o_row + (c + k0 + j) * stride * kValueDim);
+            x[j][0] = src[0];
+            x[j][1] = src[1];
+          }
+        }
+#pragma unroll
+        for (int j = 0; j < kUnroll; ++j) {
+          if (k0 + j < n) {
+            const float wk = __shfl(wl, k0 + j, 64);
+            acc[0] += wk * x[j][0].x; acc[1] += wk * x[j][0].y;
+            acc[2] += wk * x[j][0].z; acc[3] += wk * x[j][0].w;
+            acc[4] += wk * x[j][1].x; acc[5] += wk * x[j][1].y;
+            acc[6] += wk * x[j][1].z; acc[7] += wk * x[j][1].w;
+          }
+        }
+      }
+    }
+  }
   const int hpg = a.h_q / a.h_kv;
   const int t = m / hpg;
   const int h = g * hpg + m % hpg;
   const long long out_row = ((long long)b * a.s_q + t) * a.h_q + h;
-
-  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  float L = -INFINITY;
-  if (mx > -INFINITY) {
-    float sum = 0.f;
-    for (int k = 0; k < nsplit; ++k) sum += fast_exp2((a.lse_part[r0 + k * stride] - mx) * kLog2e);
-    L = mx + fast_log2(sum) * kLn2c;
-    for (int k = 0; k < nsplit; ++k) {
-      const float wk = fast_exp2((a.lse_part[r0 + k * stride] - L) * kLog2e);
-      const float4* src = reinterpret_cast<const float4*>(a.o_part + (r0 + k * stride) * kValueDim) +
-                          lane * 2;
-      const float4 x0 = src[0], x1 = src[1];
-      acc[0] += wk * x0.x; acc[1] += wk * x0.y; acc[2] += wk * x0.z; acc[3] += wk * x0.w;
-      acc[4] += wk * x1.x; acc[5] += wk * x1.y; acc[6] += wk * x1.z; acc[7] += wk * x1.w;
-    }
-  }
   uint4 pk;
   pk.x = pack_bf16(acc[0], acc[1]);
   pk.y = pack_bf16(acc[2], acc[3]);
@@ -60,8 +101,8 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
 }
 
 hipError_t launch_combine(const CombineArgs& a, hipStream_t stream) {
-  dim3 grid((a.M + 3) / 4, a.h_kv, a.batch);
-  hipLaunchKernelGGL(combine_kernel, grid, dim3(256), 0, stream, a);
+  dim3 grid((a.M + kCombineRows - 1) / kCombineRows, a.h_kv, a.batch);
+  hipLaunchKernelGGL(combine_kernel, grid, dim3(64 * kCombineRows), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -6,148 +6,180 @@
 // pages; the partition rule is this library's, stated in mla_decode.h:
 // cost-interval partition at 32-key granularity with a per-sequence fixed
 // cost, so that ragged batches spread over the compute units.
+//
+// The kernel is latency-bound (a few hundred integers), so it is built to
+// touch global memory once per input and once per output: cache_seqlens is
+// staged in LDS (up to 4096 sequences), the prefix costs C_b stay in LDS, and each part finds its
+// first and last sequence by binary search with multiplications only (the
+// part of cost position x is floor(x / T), so "part <= p" is "x < (p+1) T").
+// Integer divisions (software-emulated on the GPU) are only taken a constant
+// number of times per thread.
 #include "mla_common.hpp"
 #include "mla_internal.hpp"
 
 namespace mla {
 
-constexpr int kSchedThreads = 1024;
-
 __device__ __forceinline__ long long units_of(int n) { return ((long long)n + kStage - 1) / kStage; }
 
-// Block-wide exclusive scan of one int64 per thread; returns the prefix and
-// writes the block total to *total.
-__device__ long long block_exclusive_scan(long long v, long long* scratch, long long* total) {
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
-  long long x = v;
+// Wave-wide inclusive scan of int64.
+__device__ __forceinline__ long long wave_inclusive_scan(long long x, int lane) {
+#pragma unroll
   for (int off = 1; off < 64; off <<= 1) {
-    long long y = __shfl_up(x, off, 64);
+    const long long y = __shfl_up(x, off, 64);
     if (lane >= off) x += y;
   }
-  if (lane == 63) scratch[wave] = x;
-  __syncthreads();
-  if (wave == 0) {
-    long long w = lane < (kSchedThreads / 64) ? scratch[lane] : 0;
-    for (int off = 1; off < 16; off <<= 1) {
-      long long y = __shfl_up(w, off, 64);
-      if (lane >= off) w += y;
-    }
-    if (lane < (kSchedThreads / 64)) scratch[16 + lane] = w;
-  }
-  __syncthreads();
-  long long wave_prefix = wave > 0 ? scratch[16 + wave - 1] : 0;
-  *total = scratch[16 + kSchedThreads / 64 - 1];
-  __syncthreads();
-  return wave_prefix + x - v;
+  return x;
 }
 
-__global__ __launch_bounds__(kSchedThreads) void sched_kernel(const int32_t* __restrict__ seqlens,
-                                                              int batch, int num_parts,
-                                                              int fixed_cost,
-                                                              int32_t* __restrict__ meta,
-                                                              int32_t* __restrict__ num_splits) {
-  // C[b] = sum of cost over sequences before b; C[batch] = total.
-  __shared__ long long C[kMaxBatch + 1];
-  __shared__ long long scratch[32];
+// Block-wide exclusive scan of one int64 per thread; *total gets the sum.
+template <int NT>
+__device__ __forceinline__ long long block_exclusive_scan(long long v, long long* scratch,
+                                                          long long* total) {
   const int tid = threadIdx.x;
-  const int per = (batch + kSchedThreads - 1) / kSchedThreads;
-  const int b0 = tid * per;
+  const int lane = tid & 63, wave = tid >> 6;
+  const long long x = wave_inclusive_scan(v, lane);
+  if constexpr (NT == 64) {
+    *total = __shfl(x, 63, 64);
+    return x - v;
+  } else {
+    constexpr int NW = NT / 64;
+    if (lane == 63) scratch[wave] = x;
+    __syncthreads();
+    long long wave_prefix = 0, tot = 0;
+#pragma unroll
+    for (int i = 0; i < NW; ++i) {
+      const long long s = scratch[i];
+      if (i < wave) wave_prefix += s;
+      tot += s;
+    }
+    __syncthreads();  // scratch is reused by the next scan
+    *total = tot;
+    return wave_prefix + x - v;
+  }
+}
 
-  // 1. per-thread run of consecutive sequences: local sums, then block scan.
+template <int NT, int MAXB>
+__global__ __launch_bounds__(NT) void sched_kernel(const int32_t* __restrict__ seqlens, int batch,
+                                                   int num_parts, int fixed_cost,
+                                                   int32_t* __restrict__ meta,
+                                                   int32_t* __restrict__ num_splits) {
+  // cache_seqlens is staged in LDS unless that would not fit beside C.
+  constexpr bool kSlInLds = MAXB <= 4096;
+  __shared__ long long C[MAXB + 1];  // C[b] = cost of the sequences before b
+  __shared__ int SL_lds[kSlInLds ? MAXB : 1];
+  auto SL = [&](int b) -> int { return kSlInLds ? SL_lds[b] : seqlens[b]; };
+  __shared__ long long scratch[NT / 64];
+  const int tid = threadIdx.x;
+  const int per = (batch + NT - 1) / NT;
+  const int b0 = tid * per;
+  const long long fc = fixed_cost;
+
+  // 1. seqlens -> LDS, per-thread cost of a run of consecutive sequences.
   long long local = 0;
   for (int i = 0; i < per; ++i) {
-    int b = b0 + i;
-    if (b < batch) local += units_of(seqlens[b]) + fixed_cost;
-  }
-  long long total;
-  long long base = block_exclusive_scan(local, scratch, &total);
-  for (int i = 0; i < per; ++i) {
-    int b = b0 + i;
+    const int b = b0 + i;
     if (b < batch) {
-      C[b] = base;
-      base += units_of(seqlens[b]) + fixed_cost;
+      const int n = seqlens[b];
+      if constexpr (kSlInLds) SL_lds[b] = n;
+      local += units_of(n) + fc;
     }
   }
-  if (tid == 0) C[batch] = total;
-  __syncthreads();
-
+  long long total;
+  long long base = block_exclusive_scan<NT>(local, scratch, &total);
   long long T = (total + num_parts - 1) / num_parts;
   if (T < 1) T = 1;
 
-  // first / last part holding a piece of sequence b
-  auto first_part = [&](int b) -> long long {
-    long long u = C[b + 1] - C[b] - fixed_cost;
-    return u > 0 ? (C[b] + fixed_cost) / T : (C[b] + fixed_cost - 1) / T;
-  };
-  auto last_part = [&](int b) -> long long {
-    long long u = C[b + 1] - C[b] - fixed_cost;
-    return u > 0 ? (C[b] + fixed_cost + u - 1) / T : (C[b] + fixed_cost - 1) / T;
-  };
-
-  // 2. num_splits = exclusive prefix of pieces per sequence.
-  long long lp = 0;
+  // 2. prefix costs, and pieces per sequence = last part - first part + 1.
+  long long pieces = 0;
   for (int i = 0; i < per; ++i) {
-    int b = b0 + i;
-    if (b < batch) lp += last_part(b) - first_part(b) + 1;
+    const int b = b0 + i;
+    if (b < batch) {
+      C[b] = base;
+      const long long u = units_of(SL(b));
+      const long long first = u > 0 ? (base + fc) / T : (base + fc - 1) / T;
+      const long long last = (base + fc + u - 1) / T;
+      pieces += last - first + 1;
+      base += u + fc;
+    }
   }
+  if (tid == 0) C[batch] = total;
   long long ptotal;
-  long long pbase = block_exclusive_scan(lp, scratch, &ptotal);
+  long long pbase = block_exclusive_scan<NT>(pieces, scratch, &ptotal);
   for (int i = 0; i < per; ++i) {
-    int b = b0 + i;
+    const int b = b0 + i;
     if (b < batch) {
       num_splits[b] = (int32_t)pbase;
-      pbase += last_part(b) - first_part(b) + 1;
+      const long long cb = C[b];
+      const long long u = units_of(SL(b));
+      const long long first = u > 0 ? (cb + fc) / T : (cb + fc - 1) / T;
+      const long long last = (cb + fc + u - 1) / T;
+      pbase += last - first + 1;
     }
   }
   if (tid == 0) num_splits[batch] = (int32_t)ptotal;
+  __syncthreads();  // C complete
 
-  // 3. per part: first sequence with last_part >= p, last with first_part <= p.
-  for (int p = tid; p < num_parts; p += kSchedThreads) {
-    int lo = 0, hi = batch;  // first b with last_part(b) >= p
+  // Cost positions that decide a sequence's first and last part:
+  //   last part  = floor(KL_b / T), KL_b = C_{b+1} - 1
+  //   first part = floor(KF_b / T), KF_b = C_b + fc (or C_b + fc - 1 if empty)
+  auto KL = [&](int b) -> long long { return C[b + 1] - 1; };
+  auto KF = [&](int b) -> long long {
+    const long long cb = C[b];
+    return C[b + 1] - cb - fc > 0 ? cb + fc : cb + fc - 1;
+  };
+
+  // 3. per part: first sequence with last part >= p, last with first part <= p.
+  for (int p = tid; p < num_parts; p += NT) {
+    const long long lo_key = (long long)p * T;         // last part >= p  <=>  KL >= p T
+    const long long hi_key = (long long)(p + 1) * T;   // first part <= p <=>  KF < (p+1) T
+    int lo = 0, hi = batch;
     while (lo < hi) {
-      int mid = (lo + hi) >> 1;
-      if (last_part(mid) >= p) hi = mid; else lo = mid + 1;
+      const int mid = (lo + hi) >> 1;
+      if (KL(mid) >= lo_key) hi = mid; else lo = mid + 1;
     }
-    int bb = lo;
+    const int bb = lo;
     lo = -1;
-    hi = batch - 1;  // last b with first_part(b) <= p
+    hi = batch - 1;
     while (lo < hi) {
-      int mid = (lo + hi + 1) >> 1;
-      if (first_part(mid) <= p) lo = mid; else hi = mid - 1;
+      const int mid = (lo + hi + 1) >> 1;
+      if (KF(mid) < hi_key) lo = mid; else hi = mid - 1;
     }
-    int be = lo;
-    int32_t w[kMetaWords] = {0, 0, -1, 0, 0, 0, 0, 0};
+    const int be = lo;
+    i32x4 w0 = {0, 0, -1, 0}, w1 = {0, 0, 0, 0};
     if (bb < batch && be >= 0 && bb <= be) {
-      long long ub = C[bb + 1] - C[bb] - fixed_cost;
-      long long ue = C[be + 1] - C[be] - fixed_cost;
+      const long long ub = C[bb + 1] - C[bb] - fc;
+      const long long ue = C[be + 1] - C[be] - fc;
       long long u_begin = 0, u_end = 0;
       if (ub > 0) {
-        u_begin = (long long)p * T - C[bb] - fixed_cost;
+        u_begin = lo_key - C[bb] - fc;
         if (u_begin < 0) u_begin = 0;
       }
       if (ue > 0) {
-        u_end = (long long)(p + 1) * T - C[be] - fixed_cost;
+        u_end = hi_key - C[be] - fc;
         if (u_end > ue) u_end = ue;
       }
       long long tok_end = u_end * kStage;
-      if (tok_end > seqlens[be]) tok_end = seqlens[be];
-      w[0] = bb;
-      w[1] = (int32_t)(u_begin * kStage);
-      w[2] = be;
-      w[3] = (int32_t)tok_end;
-      w[4] = (int32_t)(p - first_part(bb));
+      if (tok_end > SL(be)) tok_end = SL(be);
+      w0 = i32x4{bb, (int32_t)(u_begin * kStage), be, (int32_t)tok_end};
+      w1.x = (int32_t)(p - KF(bb) / T);  // split index of this piece within sequence bb
     }
     i32x4* dst = reinterpret_cast<i32x4*>(meta + (long long)p * kMetaWords);
-    dst[0] = i32x4{w[0], w[1], w[2], w[3]};
-    dst[1] = i32x4{w[4], w[5], w[6], w[7]};
+    dst[0] = w0;
+    dst[1] = w1;
   }
 }
 
 hipError_t launch_sched(const int32_t* seqlens, int batch, int num_parts, int fixed_cost,
                         int32_t* meta, int32_t* num_splits, hipStream_t stream) {
-  hipLaunchKernelGGL(sched_kernel, dim3(1), dim3(kSchedThreads), 0, stream, seqlens, batch,
-                     num_parts, fixed_cost, meta, num_splits);
+  if (batch <= 64)
+    hipLaunchKernelGGL((sched_kernel<64, 64>), dim3(1), dim3(64), 0, stream, seqlens, batch,
+                       num_parts, fixed_cost, meta, num_splits);
+  else if (batch <= 1024)
+    hipLaunchKernelGGL((sched_kernel<256, 1024>), dim3(1), dim3(256), 0, stream, seqlens, batch,
+                       num_parts, fixed_cost, meta, num_splits);
+  else
+    hipLaunchKernelGGL((sched_kernel<1024, kMaxBatch>), dim3(1), dim3(1024), 0, stream, seqlens,
+                       batch, num_parts, fixed_cost, meta, num_splits);
   return hipGetLastError();
 }
 
