@@ -106,10 +106,12 @@ int mla_get_metadata_shape(int batch, int q_rows_per_kv_head, int h_kv, int *num
  *                  mla_get_metadata_shape; other values are allowed)
  *   fixed_cost     >= 1
  *   tile_metadata  device int32 [num_parts, MLA_METADATA_WORDS]: per part
- *                  {first sequence, first key of its piece, last sequence,
- *                   end key (exclusive) of its piece, split index of the
- *                   first sequence's piece, 0, 0, 0}; an empty part stores
- *                  first = 0, last = -1
+ *                  {bb = first sequence, first key of its piece,
+ *                   be = last sequence, end key (exclusive) of its piece,
+ *                   num_splits[bb] + split index of bb's piece (the partial
+ *                   slot of that piece), N_bb, N_be, num_splits[be] (the
+ *                   partial slot of be's piece, whose split index is 0)};
+ *                  an empty part stores {0, 0, -1, 0, 0, 0, 0, 0}
  *   num_splits     device int32 [batch + 1]: num_splits[0] = 0 and
  *                  num_splits[b+1] - num_splits[b] = pieces of sequence b
  * batch must be in [1, MLA_MAX_BATCH].

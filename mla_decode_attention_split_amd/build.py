@@ -22,6 +22,12 @@ COMMON = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-function",
 ]
+# Per-source device-compiler options.  The main kernel keeps its MFMA
+# accumulators in ordinary VGPRs (the rare rescale of O is then a plain
+# multiply), which leaves the AGPRs free for operands the MFMAs read directly.
+EXTRA = {
+    "decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
 
 
 def _run(cmd):
@@ -43,7 +49,7 @@ def build(verbose: bool = False) -> str:
     for s in SOURCES:
         obj = os.path.join(objdir, s.replace(".hip", ".o"))
         objs.append(obj)
-        cmds.append(["hipcc", *COMMON, "-c", os.path.join(CSRC, s), "-o", obj])
+        cmds.append(["hipcc", *COMMON, *EXTRA.get(s, []), "-c", os.path.join(CSRC, s), "-o", obj])
     with ThreadPoolExecutor(max_workers=min(4, os.cpu_count() or 1)) as ex:
         list(ex.map(_run, cmds))
     tmp = LIB + ".tmp"

@@ -155,6 +155,11 @@ int prepare_decode(const void* q, const void* blocked_k, const int32_t* block_ta
   if (M_ll > MLA_MAX_ROWS)
     return fail(MLA_ERR_UNSUPPORTED, "s_q * h_q / h_kv = %lld > %d", M_ll, MLA_MAX_ROWS);
   const int M = (int)M_ll;
+  // the kernel addresses one sequence's queries and one 32-key stage through
+  // 32-bit buffer ranges
+  if ((long long)s_q * h_q * MLA_HEAD_DIM * 2 >= 0x7fffffffLL ||
+      32LL * h_kv * MLA_HEAD_DIM * 2 >= 0x7fffffffLL)
+    return fail(MLA_ERR_UNSUPPORTED, "s_q * h_q = %lld or h_kv = %d too large", (long long)s_q * h_q, h_kv);
   int rc = check_rows(M, h_kv);
   if (rc != MLA_OK) return rc;
   if (num_pages < 1 || max_blocks_per_seq < 1)

@@ -11,22 +11,35 @@
 // partial outputs).
 //
 // Design (gfx950):
-//   * 4 waves per workgroup, one workgroup per CU (147 KB LDS ring).
-//   * Keys stream through a ring of 4 LDS slots of 32 keys (36 KB each) with
-//     16-byte direct global->LDS loads; 3 stages are in flight while one is
-//     computed.  Rows are XOR-swizzled in 16-byte chunks (conflict-free).
-//   * Each wave owns R query rows (R = 16 or 32).  Scores are computed
-//     transposed, S^T = K Q^T, with K from LDS (A operand) and Q^T resident in
-//     registers (B operand); the MFMA result is then already laid out as the
-//     B operand P^T of O^T = V^T P^T.  V^T comes from LDS through transposed
-//     8-byte reads (ds_read_b64_tr_b16), so V needs no copy of its own.
+//   * 4 waves per workgroup, one workgroup per CU.  The part's stages (query
+//     rows, then 32-key blocks, per piece) stream through a ring of 4 LDS
+//     slots of 36 KB with 16-byte buffer loads straight into LDS.  Every ring
+//     position is loaded with the same number of instructions; lanes with
+//     nothing to load address past their buffer's range, which costs no
+//     memory traffic, so the per-stage waits are exact constants.
+//   * The prologue needs one memory trip after the part's metadata record:
+//     the record carries the lengths and partial slots of the part's first
+//     and last sequence, and the page indices of the part are loaded into
+//     registers (lane i holds entry i) while the query stage is already in
+//     flight.
+//   * Each wave owns R query rows (R = 16 or 32) and 512 / DG value dims.
+//     Scores are computed transposed, S^T = K Q^T, with K from LDS (A
+//     operand) and Q^T resident in registers (B operand); the MFMA result is
+//     already laid out as the B operand P^T of O^T = V^T P^T.  V^T comes from
+//     LDS through transposed 8-byte reads (ds_read_b64_tr_b16).
+//   * Split-K scores: the DG waves of a row group each contract an interleaved
+//     share of the 576 dims (and, with DG = 4, one of the two 16-key blocks),
+//     then exchange fp32 partial scores through LDS and add them in a fixed
+//     order, so every wave of the group holds bit-identical scores.
+//   * Software pipeline: in the iteration of key block s a wave computes the
+//     partial scores of block s while it finishes block s - 1 (partial-score
+//     sum, softmax, P V); the MFMAs of one overlap the vector work of the
+//     other, and one barrier per stage serves both the ring and the exchange.
 //   * Softmax in fp32 in the log2 domain; the running max is raised only when
 //     a row's new max exceeds it by more than kTau (then O and l are
-//     rescaled), so most stages skip the rescale.  P is rounded to bf16 for
-//     the MFMA and the row sum adds the rounded values, so normalisation uses
-//     exactly the weights that multiplied V.
-//   * Waves of one row group (DG > 1) split the 512 value dims; each repeats
-//     the cheap score MFMAs of its rows, so no cross-wave merge is needed.
+//     rescaled).  P is rounded to bf16 for the MFMA and a second row sum adds
+//     the rounded values, so the output is normalised by exactly the weights
+//     that multiplied V.
 #include <type_traits>
 
 #include "mla_common.hpp"
@@ -37,17 +50,31 @@ namespace mla {
 constexpr float kTau = 8.0f;        // lazy-rescale threshold (log2 units)
 constexpr float kMinit = -1.0e30f;  // finite "minus infinity" for the running max
 constexpr float kLn2 = 0.69314718055994530942f;
+constexpr int kListPages = 128;     // page indices held in registers (2 per lane)
+constexpr int kListPieces = 64;     // sequence lengths held in registers (1 per lane)
+constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, 32-bit data format
+constexpr unsigned kOutOfRange = 0x80000000u;  // buffer offset that loads nothing
 
 __device__ __forceinline__ i16x8 lds_read_b128(const char MLA_LDS* p) {
   return *reinterpret_cast<const i16x8 MLA_LDS*>(p);
 }
+__device__ __forceinline__ f32x4 lds_read_f4(const char MLA_LDS* p) {
+  return *reinterpret_cast<const f32x4 MLA_LDS*>(p);
+}
+__device__ __forceinline__ void lds_write_f4(char MLA_LDS* p, f32x4 v) {
+  *reinterpret_cast<f32x4 MLA_LDS*>(p) = v;
+}
 __device__ __forceinline__ i16x4 lds_read_tr(const char MLA_LDS* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((i16x4 MLA_LDS*)(p));
 }
-// 16-byte global -> LDS copy per lane; the LDS address of lane l is dst + 16 l.
-__device__ __forceinline__ void load_lds16(const char* src, char MLA_LDS* dst) {
-  __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)src,
-                                   (void MLA_LDS*)dst, 16, 0, 0);
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, kRsrcWord3);
+}
+// 16 bytes from rsrc + voff into LDS; lane l writes dst + 16 l.  An offset
+// past the buffer's range loads nothing (the LDS bytes become zero).
+__device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t r, unsigned voff,
+                                           char MLA_LDS* dst) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (void MLA_LDS*)dst, 16, voff, 0, 0, 0);
 }
 __device__ __forceinline__ f32x16 mfma32(i16x8 a, i16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
@@ -57,28 +84,22 @@ __device__ __forceinline__ f32x4 mfma16(i16x8 a, i16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
+__device__ __forceinline__ int readlane(int v, int lane) { return __builtin_amdgcn_readlane(v, lane); }
+// max of x over lanes l and l ^ 32 (v_permlane32_swap), and l ^ 16
+__device__ __forceinline__ float max_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float max_xor16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
 
-// Large accumulators (32-row tiles, 256 registers) stay in AGPRs: element
-// reads/writes go through accvgpr moves so the compiler never moves a whole
-// accumulator into VGPRs.  Small ones are ordinary registers.
-template <bool PIN>
-__device__ __forceinline__ float acc_read(float x) {
-  if constexpr (!PIN) return x;
-  float v;
-  asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(v) : "a"(x));
-  return v;
-}
-template <bool PIN>
-__device__ __forceinline__ float acc_write(float v) {
-  if constexpr (!PIN) return v;
-  float x;
-  asm volatile("v_accvgpr_write_b32 %0, %1" : "=a"(x) : "v"(v));
-  return x;
-}
-template <bool PIN, int N, typename V>
+// o *= s (the rescale when a row's running max is raised).
+template <int N, typename V>
 __device__ __forceinline__ void acc_scale(V& o, float s) {
 #pragma unroll
-  for (int i = 0; i < N; ++i) o[i] = acc_write<PIN>(acc_read<PIN>(o[i]) * s);
+  for (int i = 0; i < N; ++i) o[i] *= s;
 }
 
 __device__ __forceinline__ i16x8 cat(i16x4 a, i16x4 b) {
@@ -94,8 +115,7 @@ __device__ __forceinline__ i16x4 zero_from(i16x4 v, int first_bad) {
 
 // exp2 of K masked scores -> packed bf16 B operand.  Adds the fp32 weights to
 // *l (the softmax denominator behind lse) and the bf16-rounded weights to *lr
-// (the normaliser of out, so out is an exact weighted mean of V with the
-// weights the MFMA used).
+// (the normaliser of out).
 template <int K>
 __device__ __forceinline__ void weights_bf16(const float* x, float m, uint32_t* packed, float* l,
                                              float* lr) {
@@ -112,47 +132,82 @@ __device__ __forceinline__ void weights_bf16(const float* x, float m, uint32_t* 
   *lr += rsum;
 }
 
+// Wave-wide exclusive prefix sum of an int.
+__device__ __forceinline__ int wave_exclusive_sum(int v, int lane) {
+  int x = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(x, off, 64);
+    if (lane >= off) x += y;
+  }
+  return x - v;
+}
+
+// Tile shape.  R rows per wave (32x32x16 MFMA for R = 32, 16x16x32 for
+// R = 16), RG row groups x DG value-dim groups = 4 waves.
 template <int R, int RG, int DG>
+struct Tile {
+  static constexpr int NW = RG * DG;
+  static constexpr int BM = R * RG;                      // query rows per workgroup
+  static constexpr int LPW = kLoadsPerStage / NW;        // 16-byte loads per lane per stage
+  static constexpr int KSTEPS = R == 32 ? 36 : 18;       // score k-steps over 576 dims
+  static constexpr int KSPLIT = 2;                       // k-step interleave among DG waves
+  static constexpr int KBSPLIT = DG / KSPLIT;            // 16-key blocks split among waves (R = 16)
+  static constexpr int KS_W = KSTEPS / KSPLIT;           // k-steps per wave
+  static constexpr int KB_W = R == 32 ? 1 : 2 / KBSPLIT; // score blocks per wave
+  static constexpr int NT = (R == 32 ? 16 : 32) / DG;    // value-dim tiles per wave
+  static constexpr int OREGS = R == 32 ? 16 : 4;         // accumulator registers per tile
+  static constexpr int PARTIAL_BYTES = R == 32 ? 4096 : 1024;  // one score block, fp32
+  static constexpr int XCH_ONE = NW * KB_W * PARTIAL_BYTES;    // one exchange buffer
+  // 16-row tiles double-buffer the exchange; 32-row tiles have room for one
+  // buffer and separate its reads from the next writes with a barrier.
+  static constexpr int XCH_BUFS = R == 32 ? 1 : 2;
+  static constexpr int NQ = (BM + kStage - 1) / kStage;  // query stages per piece
+  static constexpr int QK_MFMA = KS_W * KB_W;
+  static constexpr int PV_MFMA = R == 32 ? 2 * NT : NT;
+  static constexpr int NSLOT = QK_MFMA + PV_MFMA;        // points where loads are issued
+  static_assert(NW == kWaves, "four waves per workgroup");
+  static_assert(DG >= 2 && DG % 2 == 0, "split-K tiles only");
+  static_assert(LPW * NW == kLoadsPerStage, "stage loads split evenly");
+  static_assert(KS_W * KSPLIT == KSTEPS && KBSPLIT * KSPLIT == DG, "score split");
+  static_assert(R == 16 || KBSPLIT == 1, "key-block split only for 16-row tiles");
+  static_assert(NSLOT >= LPW, "one load per issue point at most");
+  static_assert(2 * LPW < 63, "vector memory counter capacity");
+  static_assert(kLdsBytes + XCH_BUFS * XCH_ONE <= 163840, "LDS capacity");
+};
+
+template <int R, int RG, int DG, bool QG>
 __global__ __launch_bounds__(256, 1) void decode_kernel(
     const uint16_t* __restrict__ q_ptr, const uint16_t* __restrict__ kv_ptr,
     const int32_t* __restrict__ block_table, const int32_t* __restrict__ seqlens,
-    const int32_t* __restrict__ meta, const int32_t* __restrict__ num_splits,
-    uint16_t* __restrict__ out, float* __restrict__ lse, float* __restrict__ o_part,
-    float* __restrict__ lse_part, DecodeArgs a) {
-  // The pointers are restrict-qualified kernel parameters so that uniform reads
-  // of the read-only metadata become scalar loads (their waits never touch the
-  // vector-memory counter that tracks the staged keys).
-  constexpr int NW = RG * DG;
-  static_assert(NW == kWaves, "four waves per workgroup");
-  constexpr int BM = R * RG;
-  constexpr int LPW = kLoadsPerStage / NW;  // 16-byte loads per lane per stage
-  static_assert(LPW * NW == kLoadsPerStage, "stage loads split evenly");
-  // R = 32: 32x32x16 MFMA tiles; R = 16: 16x16x32 tiles.
-  constexpr int KSTEPS = R == 32 ? 36 : 18;     // score k-steps over 576 dims
-  constexpr int NT = (R == 32 ? 16 : 32) / DG;  // value-dim tiles per wave
-  constexpr int OREGS = R == 32 ? 16 : 4;       // accumulator registers per tile
-  static_assert(3 * LPW + KSTEPS <= 63, "vector memory counter capacity");
+    const int32_t* __restrict__ meta, uint16_t* __restrict__ out, float* __restrict__ lse,
+    float* __restrict__ o_part, float* __restrict__ lse_part, DecodeArgs a) {
+  using T = Tile<R, RG, DG>;
+  constexpr int NW = T::NW, BM = T::BM, LPW = T::LPW, KS_W = T::KS_W, KB_W = T::KB_W;
+  constexpr int NT = T::NT, OREGS = T::OREGS, NQ = T::NQ;
   using OAcc = typename std::conditional<R == 32, f32x16, f32x4>::type;
-  constexpr bool kPin = R == 32;             // pin the 256-register accumulators to AGPRs
-  constexpr int NQ = (BM + kStage - 1) / kStage;  // query stages (32 rows each) per piece
+  constexpr int SREGS = R == 32 ? 16 : 8;  // scores per lane per stage
 
-  __shared__ __attribute__((aligned(1024))) char lds_raw[kLdsBytes];
+  __shared__ __attribute__((aligned(1024))) char lds_raw[kLdsBytes + T::XCH_BUFS * T::XCH_ONE];
   char MLA_LDS* lds = (char MLA_LDS*)lds_raw;
+  char MLA_LDS* xch0 = lds + kLdsBytes;
 
   const int tid = threadIdx.x;
   const int w = tid >> 6;
   const int lane = tid & 63;
   const int rg = w / DG;
   const int dg = w % DG;
+  const int kh = dg % T::KSPLIT;   // k-step share: steps ks = 2 j + kh
+  const int kbs = dg / T::KSPLIT;  // key block of this wave when KBSPLIT = 2
 
   // ---- which part / row tile / KV head -------------------------------------
   const int inner = a.m_tiles * a.h_kv;
   int part, inner_idx;
-  if (a.xcd_map) {
+  if (a.xcd_map) {  // the m-tiles and KV heads of a part run on one XCD
     const int id = blockIdx.x;
-    const int j = id >> 3;
-    inner_idx = j % inner;
-    part = (j / inner) * 8 + (id & 7);
+    const int jj = id >> 3;
+    inner_idx = jj % inner;
+    part = (jj / inner) * 8 + (id & 7);
   } else {
     part = blockIdx.x / inner;
     inner_idx = blockIdx.x % inner;
@@ -160,40 +215,96 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(
   const int mtile = inner_idx / a.h_kv;
   const int g = inner_idx % a.h_kv;
   const int32_t* mp = meta + (long long)part * kMetaWords;
-  const int bb = mp[0], tb = mp[1], be = mp[2], te = mp[3], k0 = mp[4];
+  const int bb = mp[0], tb = mp[1], be = mp[2], te = mp[3];
+  const int slot_first = mp[4], n_first = mp[5], n_last = mp[6], slot_last = mp[7];
   if (bb > be) return;  // empty part (uniform over the workgroup)
 
   const int M = a.M;
   const int hpg = a.h_q / a.h_kv;
   const int row_stride = a.h_kv * kRowBytes;  // bytes between consecutive tokens
   const char* kv_bytes = reinterpret_cast<const char*>(kv_ptr) + (long long)g * kRowBytes;
+  const int npieces = be - bb + 1;
+  const int m_lo = mtile * BM;
+  const int m_hi = (m_lo + BM < M ? m_lo + BM : M);  // end of the tile's valid rows
+
+  // ---- the part's pages, one per lane --------------------------------------
+  // Piece j (sequence bb + j) covers keys [lo_j, hi_j); its pages are entries
+  // lo_j / 64 .. ceil(hi_j / 64) - 1 of the sequence's block_table row and
+  // occupy positions cum_j .. cum_j + pages_j - 1 of the part's page list.
+  // With one or two pieces the metadata record holds every length needed, so
+  // the page loads are the prologue's only memory trip; longer parts first
+  // load the lengths of their middle sequences.
+  int v_n = 0;  // lane j: length of sequence bb + j (middle pieces only)
+  const bool short_part = npieces <= 2;
+  if (!short_part) {
+    if (lane < npieces && lane < kListPieces) v_n = seqlens[bb + lane];
+    asm volatile("" ::"v"(v_n));
+  }
+  auto piece_n = [&](int j) -> int {
+    if (j == 0) return n_first;
+    if (j == npieces - 1) return n_last;
+    return j < kListPieces ? readlane(v_n, j) : sload_i32(seqlens + bb + j);
+  };
+  int v_pages = 0;
+  {
+    const int j = lane;
+    if (j < npieces && j < kListPieces) {
+      const int lo = j == 0 ? tb : 0;
+      const int hi = bb + j == be ? te : (j == 0 ? n_first : v_n);
+      v_pages = hi > lo ? (hi + kPage - 1) / kPage - lo / kPage : 0;
+    }
+  }
+  const int v_cum = wave_exclusive_sum(v_pages, lane);
+  const int listed_pieces = npieces < kListPieces ? npieces : kListPieces;
+  const int total_listed = readlane(v_cum, listed_pieces - 1) + readlane(v_pages, listed_pieces - 1);
+  // The page list is used only if it holds every page of the part.
+  const bool use_list = npieces <= kListPieces && total_listed <= kListPages;
+  int v_page[2] = {0, 0};
+  if (use_list) {
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const int i = lane + 64 * half;
+      long long idx = -1;
+      for (int j = 0; j < listed_pieces; ++j) {
+        const int c = readlane(v_cum, j), p = readlane(v_pages, j);
+        if (i >= c && i < c + p) idx = (long long)(bb + j) * a.max_blocks + (j == 0 ? tb : 0) / kPage + (i - c);
+      }
+      if (idx >= 0) v_page[half] = block_table[idx];
+    }
+  }
 
   // ---- lane constants --------------------------------------------------------
   const int lr = lane % R;  // this lane's query row inside the wave tile
-  const int my_row = mtile * BM + rg * R + lr;
+  const int my_row = m_lo + rg * R + lr;
   const int q_row = my_row < M ? my_row : M - 1;
   const int q_t = q_row / hpg;
   const int q_h = g * hpg + q_row % hpg;
 
-  // Byte offset (inside a stage) of this lane's k-th 16-byte global load.
-  auto load_off = [&](int k) {
-    const int s = (k * NW + w) * 64 + lane;  // 16-byte LDS cell filled by this lane
+  // Byte offset (inside a stage) of this lane's k-th 16-byte load, and of the
+  // LDS cell it fills (wave w's k-th load fills cells (k NW + w) 64 + lane).
+  unsigned loff[LPW];
+#pragma unroll
+  for (int k = 0; k < LPW; ++k) {
+    const int s = (k * NW + w) * 64 + lane;
     const int row = s / kChunksPerRow;
     const int pc = s - row * kChunksPerRow;
-    return row * row_stride + phys_chunk<R>(row, pc) * 16;  // swizzle is an involution
-  };
+    loff[k] = row * row_stride + phys_chunk<R>(row, pc) * 16;  // the swizzle is an involution
+  }
 
-  // K (A operand) LDS offsets and V^T (transposed read) offsets inside a stage.
-  // K: lane reads 16 B of key row `row`, chunk c; stored at chunk c ^ swz(row).
-  // V^T: a 16-lane group reads 4 key rows x 16 value dims; lane 4r + c supplies
-  // the address of row r, dims 4c..4c+3 (8 B) and receives one dim of all 4.
-  int koff[R == 32 ? 4 : 2];
+  // K / Q fragment offsets (A / B operands) for this wave's k-steps, and V^T
+  // (transposed read) offsets, inside a stage.  Local step j is k-step
+  // ks = 2 j + kh.
+  //   R = 32: chunk 2 ks + h (h = lane / 32) -> koff[j % 2] + 128 (j / 2)
+  //   R = 16: chunk 4 ks + lane / 16         -> koff[0] + 128 j
+  int koff[2];
   int voff[4];
   if constexpr (R == 32) {
     const int h = lane >> 5;
-    // chunk of k-step ks = 8 (ks >> 2) + 2 (ks & 3) + h
+    int kbase[4];
 #pragma unroll
-    for (int rr = 0; rr < 4; ++rr) koff[rr] = lr * kRowBytes + 16 * ((2 * rr + h) ^ swz<32>(lr));
+    for (int rr = 0; rr < 4; ++rr) kbase[rr] = lr * kRowBytes + 16 * ((2 * rr + h) ^ swz<32>(lr));
+    koff[0] = kh ? kbase[1] : kbase[0];
+    koff[1] = kh ? kbase[3] : kbase[2];
     // key row 16 kb + 8 jh + 4 h + r: swz = 4 (r >> 1) + 2 h + jh;
     // dims 32 nb + 16 dh + 4 c: chunk 8 (nb >> 1) + 4 (nb & 1) + 2 dh + (c >> 1)
     const int G = lane >> 4, i = lane & 15, dh = G & 1, r = i >> 2, c = i & 3;
@@ -205,9 +316,7 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(
                              16 * ((4 * nbp + 2 * dh + (c >> 1)) ^ (4 * (r >> 1) + 2 * h + jh));
   } else {
     const int gq = lane >> 4;
-    // chunk of k-step ks = 8 (ks >> 1) + 4 (ks & 1) + gq
-#pragma unroll
-    for (int rr = 0; rr < 2; ++rr) koff[rr] = lr * kRowBytes + 16 * ((4 * rr + gq) ^ swz<16>(lr));
+    koff[0] = koff[1] = lr * kRowBytes + 16 * ((4 * kh + gq) ^ swz<16>(lr));
     // key row 16 jh + 4 gq + r: swz = 4 (gq & 1) + r;
     // dims 16 nb + 4 c: chunk 8 (nb >> 2) + 2 (nb & 3) + (c >> 1)
     const int i = lane & 15, r = i >> 2, c = i & 3;
@@ -216,85 +325,140 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(
       voff[nbq] = (4 * gq + r) * kRowBytes + 8 * (c & 1) +
                   16 * ((2 * nbq + (c >> 1)) ^ (4 * (gq & 1) + r));
   }
+  auto kstep_off = [&](int j) -> int {
+    if constexpr (R == 32) return koff[j & 1] + 128 * (j >> 1);
+    else return koff[0] + 128 * j;
+  };
+  // Key index (within a stage) of score register i of this lane is
+  // key_lane + key_reg(i): a per-lane part and a compile-time part, so masks
+  // compare against immediates.
+  const int key_lane = R == 32 ? 4 * (lane >> 5) : 4 * (lane >> 4);
+  auto key_reg = [](int i) -> int { return R == 32 ? 8 * (i >> 2) + (i & 3) : 16 * (i >> 2) + (i & 3); };
 
   // ---- stage stream -----------------------------------------------------------
-  // For every non-empty piece of the part: NQ query stages (32 query rows of
-  // the tile each, same swizzled row layout as the keys), then the piece's key
-  // stages.  Everything goes global -> LDS through the same ring, so the only
-  // vector-memory waits are the explicit per-stage ones below.
-  const int m_hi = (mtile * BM + BM < M ? mtile * BM + BM : M);  // end of the tile's valid rows
-  int lb = bb, lq = 0, ltok = tb, lhi = (bb == be) ? te : seqlens[bb];
+  // For every non-empty piece: NQ query stages (32 rows of the tile each, same
+  // swizzled row layout as the keys), then the piece's key stages.  Stream
+  // position c uses ring slot c % 4; position c + 2 is loaded while position c
+  // is computed.  Past the end of the stream the loads are out of range.
+  int lj = 0, lq = 0, ltok = tb, lhi = (bb == be) ? te : n_first, lpg = 0;
   bool lvalid = true;
   auto next_piece = [&]() {
     while (true) {
-      if (lb >= be) {
+      if (bb + lj >= be) {
         lvalid = false;
         return;
       }
-      ++lb;
+      const int lo_cur = lj == 0 ? tb : 0;  // step over the pages of the piece left
+      if (lhi > lo_cur) lpg += (lhi + kPage - 1) / kPage - lo_cur / kPage;
+      ++lj;
       lq = 0;
       ltok = 0;
-      lhi = (lb == be) ? te : sload_i32(seqlens + lb);
+      lhi = (bb + lj == be) ? te : piece_n(lj);
       if (ltok < lhi) return;
     }
   };
   if (ltok >= lhi) next_piece();
-  int issued = 0;
-  // Issue the next stage of the stream into ring slot `wr` (= slot issued % 4).
-  auto issue = [&](char MLA_LDS* __restrict__ wr) {
-    if (!lvalid) return;
-    char MLA_LDS* dst = wr + w * 1024;
-    if (lq < NQ) {
-      const char* qbase = reinterpret_cast<const char*>(q_ptr);
+
+  // The stream position being loaded: a buffer over its bytes (range 0 =
+  // nothing, past the end of the stream) and per-lane offsets (the key-row
+  // offsets loff, or query-row offsets for a query stage).
+  __amdgpu_buffer_rsrc_t pend = make_rsrc(kv_bytes, 0);
+  char MLA_LDS* pend_dst = lds;
+  // Query stages: with one KV head the 32 rows of a query stage are
+  // consecutive q rows, so they load with the key-row offsets loff from a
+  // buffer that starts at the stage's first row and ends at the tile's last
+  // valid row.  Otherwise (QG) every lane's offset is computed.
+  bool pend_q = false;
+  unsigned qoff[QG ? LPW : 1];
+  auto fire = [&](int k) {
+    if constexpr (QG) load_lds16(pend, pend_q ? qoff[k] : loff[k], pend_dst + k * NW * 1024);
+    else load_lds16(pend, loff[k], pend_dst + k * NW * 1024);
+  };
+  auto fire_all = [&]() {
 #pragma unroll
-      for (int k = 0; k < LPW; ++k) {
-        const int cell = (k * NW + w) * 64 + lane;
-        const int row = cell / kChunksPerRow;
-        const int pc = cell - row * kChunksPerRow;
-        int m = mtile * BM + kStage * lq + row;
-        m = m < m_hi ? m : m_hi - 1;
-        const int t = m / hpg;
-        const long long qrow = ((long long)lb * a.s_q + t) * a.h_q + g * hpg + (m - t * hpg);
-        load_lds16(qbase + qrow * kRowBytes + phys_chunk<R>(row, pc) * 16, dst + k * NW * 1024);
+    for (int k = 0; k < LPW; ++k) fire(k);
+  };
+  // issue point s of the stage's NSLOT points fires loads k with
+  // k * NSLOT / LPW == s (resolved at compile time)
+  auto fire_slot = [&](int s) {
+#pragma unroll
+    for (int k = 0; k < LPW; ++k)
+      if (k * T::NSLOT / LPW == s) fire(k);
+  };
+  // the loads of issue points from..NSLOT-1
+  auto fire_from = [&](int from) {
+#pragma unroll
+    for (int k = 0; k < LPW; ++k)
+      if (k * T::NSLOT / LPW >= from) fire(k);
+  };
+  // Plan the next stream position into ring slot `wr`; the caller fires its
+  // LPW loads.
+  auto plan = [&](char MLA_LDS* __restrict__ wr) {
+    pend_dst = wr + w * 1024;
+    pend_q = false;
+    if (lvalid && lq < NQ) {
+      const int b = bb + lj;
+      const char* qseq = reinterpret_cast<const char*>(q_ptr) + (long long)b * a.s_q * a.h_q * kRowBytes;
+      const int m0 = m_lo + kStage * lq;
+      if constexpr (QG) {
+        pend = make_rsrc(qseq, a.s_q * a.h_q * kRowBytes);
+        pend_q = true;
+#pragma unroll
+        for (int k = 0; k < LPW; ++k) {
+          const int cell = (k * NW + w) * 64 + lane;
+          const int row = cell / kChunksPerRow;
+          const int pc = cell - row * kChunksPerRow;
+          const int m = m0 + row;
+          const int t = m / hpg;
+          qoff[k] = m < m_hi ? (unsigned)((t * a.h_q + g * hpg + (m - t * hpg)) * kRowBytes +
+                                          phys_chunk<R>(row, pc) * 16)
+                             : kOutOfRange;
+        }
+      } else {
+        int rows = m_hi - m0 < kStage ? m_hi - m0 : kStage;
+        rows = rows > 0 ? rows : 0;  // the tile's last query stage may be empty
+        pend = make_rsrc(qseq + (long long)m0 * kRowBytes, rows * kRowBytes);
       }
       ++lq;
-    } else {
-      const int page = sload_i32(block_table + (long long)lb * a.max_blocks + (ltok >> 6));
-      const char* src = kv_bytes + ((long long)page * kPage + (ltok & 63)) * row_stride;
-#pragma unroll
-      for (int k = 0; k < LPW; ++k) load_lds16(src + load_off(k), dst + k * NW * 1024);
+    } else if (lvalid) {
+      const int pidx = lpg + (ltok >> 6) - (lj == 0 ? tb : 0) / kPage;  // position in the page list
+      int page;
+      if (use_list) page = readlane(pidx < 64 ? v_page[0] : v_page[1], pidx & 63);
+      else page = sload_i32(block_table + (long long)(bb + lj) * a.max_blocks + (ltok >> 6));
+      pend = make_rsrc(kv_bytes + ((long long)page * kPage + (ltok & 63)) * row_stride,
+                       kStage * row_stride);
       ltok += kStage;
       if (ltok >= lhi) next_piece();
+    } else {
+      pend = make_rsrc(kv_bytes, 0);
     }
-    ++issued;
   };
-  issue(lds);
-  issue(lds + kStageBytes);
-  issue(lds + 2 * kStageBytes);
+  plan(lds);
+  fire_all();
+  plan(lds + kStageBytes);
+  fire_all();
 
   int cstage = 0;
-  // wait for stage `cstage` (the ones issued after it may stay in flight), then
-  // a barrier: the stage is visible to all waves and the slot refilled next
-  // has been read by everyone
+  auto slot_of = [&](int c) { return lds + (c & (kSlots - 1)) * kStageBytes; };
+  // Wait for stream position cstage (position cstage + 1 may stay in flight),
+  // then a barrier: the stage and the previous iteration's partial scores are
+  // visible to all waves, and the slot refilled next has been read by all.
   auto stage_ready = [&]() {
-    const int ahead = issued - 1 - cstage;
-    if (ahead >= 2) wait_vmcnt<2 * LPW>();
-    else if (ahead == 1) wait_vmcnt<LPW>();
-    else wait_vmcnt<0>();
+    wait_vmcnt<LPW>();
     block_barrier();
   };
   // query rows of this wave inside its query stage
   const int q_stage = (rg * R) / kStage;
   const int q_row0 = (rg * R) % kStage;
 
-  for (int b = bb; b <= be; ++b) {
-    const int N = sload_i32(seqlens + b);
-    const int lo = (b == bb) ? tb : 0;
+  for (int j = 0; j < npieces; ++j) {
+    const int b = bb + j;
+    const int N = piece_n(j);
+    const int lo = (j == 0) ? tb : 0;
     const int hi = (b == be) ? te : N;
     const int nst = hi > lo ? (hi - lo + kStage - 1) / kStage : 0;
-    const int s0 = sload_i32(num_splits + b);
-    const int nsplit = sload_i32(num_splits + b + 1) - s0;
-    const int split_k = (b == bb) ? k0 : 0;
+    const bool whole = lo == 0 && hi == N;  // the piece is the whole sequence
+    const int slot = j == 0 ? slot_first : slot_last;  // partial slot (pieces of split sequences)
     int row_lim = a.causal ? N - a.s_q + q_t + 1 : N;
     if (row_lim > N) row_lim = N;
     // keys every row of the workgroup sees (row t = 0 has the fewest)
@@ -304,88 +468,48 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) o[nt] = OAcc{};
     float m_run = kMinit, l_run = 0.f, lr_run = 0.f;
-    i16x8 qf[KSTEPS];
+    i16x8 qf[KS_W];
 
-    if (nst > 0) {
-      for (int j = 0; j < NQ; ++j, ++cstage) {
-        stage_ready();
-        // rd (this stage) and wr (the slot refilled now) are different slots
-        [&](const char MLA_LDS* __restrict__ rd, char MLA_LDS* __restrict__ wr) {
-        issue(wr);
-        if (j == q_stage) {
-          const char MLA_LDS* st = rd + q_row0 * kRowBytes;
-          if constexpr (R == 32) {
-#pragma unroll
-            for (int ks = 0; ks < KSTEPS; ++ks)
-              qf[ks] = lds_read_b128(st + koff[ks & 3] + 128 * (ks >> 2));
-          } else {
-#pragma unroll
-            for (int ks = 0; ks < KSTEPS; ++ks)
-              qf[ks] = lds_read_b128(st + koff[ks & 1] + 128 * (ks >> 1));
-          }
-        }
-        }(lds + (cstage & (kSlots - 1)) * kStageBytes, lds + ((cstage + 3) & (kSlots - 1)) * kStageBytes);
-      }
-    }
-
-    for (int s = 0; s < nst; ++s, ++cstage) {
-      stage_ready();
-      // rd (this stage) and wr (the slot refilled now) are different slots
-      [&](const char MLA_LDS* __restrict__ rd, char MLA_LDS* __restrict__ wr) {
-      issue(wr);
-
-      const char MLA_LDS* st = rd;
-      const int tok0 = lo + s * kStage;
+    // Finish key stage sp of this piece (ring slot `st`): softmax of the full
+    // scores sc and O^T += V^T P^T.  Loads for the stage in flight are fired
+    // at issue points first_slot.. of the stage's schedule.
+    auto finish = [&](const float* sc, int sp, const char MLA_LDS* st, int first_slot) {
+      const int tok0 = lo + sp * kStage;
       const int nvalid = N - tok0 < kStage ? N - tok0 : kStage;
       const bool tail = nvalid < kStage;
       const bool full = tok0 + kStage <= lim_all;  // no key of the stage is masked
-
+      float x[SREGS];
+#pragma unroll
+      for (int i = 0; i < SREGS; ++i) x[i] = sc[i] * a.scale_log2;
+      if (!full) {
+        const int lim = ((row_lim - tok0 < nvalid) ? row_lim - tok0 : nvalid) - key_lane;
+#pragma unroll
+        for (int i = 0; i < SREGS; ++i) x[i] = key_reg(i) < lim ? x[i] : -INFINITY;
+      }
+      float mx = x[0];
+#pragma unroll
+      for (int i = 1; i < SREGS; ++i) mx = fmaxf(mx, x[i]);
+      if constexpr (R == 16) mx = max_xor16(mx);
+      mx = max_xor32(mx);
+      // Raise the running max only when some row's max exceeds it by more
+      // than kTau; O is then rescaled tile by tile just before its next MFMA.
+      const bool rescale = __any(mx > m_run + kTau);
+      float alpha = 1.f;
+      if (rescale) {
+        const float m_new = fmaxf(m_run, mx);
+        alpha = fast_exp2(m_run - m_new);
+        m_run = m_new;
+        l_run *= alpha;
+        lr_run *= alpha;
+      }
+      uint32_t pw[SREGS / 2];
+      weights_bf16<SREGS>(x, m_run, pw, &l_run, &lr_run);
+      const int nv_lane = nvalid - key_lane;  // valid keys past this lane's first key
       if constexpr (R == 32) {
-        const int h = lane >> 5;
-        // ---- scores S^T [32 keys x 32 rows]: rolling prefetch of K fragments ----
-        constexpr int KP = 4;
-        i16x8 kf[KP];
-#pragma unroll
-        for (int j = 0; j < KP; ++j) kf[j] = lds_read_b128(st + koff[j & 3] + 128 * (j >> 2));
-        f32x16 sa = {};
-#pragma unroll
-        for (int ks = 0; ks < KSTEPS; ++ks) {
-          sa = mfma32(kf[ks % KP], qf[ks], sa);
-          if (ks + KP < KSTEPS)
-            kf[ks % KP] = lds_read_b128(st + koff[(ks + KP) & 3] + 128 * ((ks + KP) >> 2));
-          __builtin_amdgcn_sched_barrier(0);
-        }
-        // ---- online softmax (lane: row lr, 16 keys) ----
-        float x[16];
-        float mx = -INFINITY;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) x[i] = sa[i] * a.scale_log2;
-        if (!full) {
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int tk = 8 * (i >> 2) + 4 * h + (i & 3);
-            x[i] = (tk < nvalid && tok0 + tk < row_lim) ? x[i] : -INFINITY;
-          }
-        }
-#pragma unroll
-        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, x[i]);
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        if (__any(mx > m_run + kTau)) {
-          const float m_new = fmaxf(m_run, mx);
-          const float alpha = fast_exp2(m_run - m_new);
-          m_run = m_new;
-          l_run *= alpha;
-          lr_run *= alpha;
-#pragma unroll
-          for (int nt = 0; nt < NT; ++nt) acc_scale<kPin, OREGS>(o[nt], alpha);
-        }
-        uint32_t pw[8];
-        weights_bf16<16>(x, m_run, pw, &l_run, &lr_run);
         const i16x8 pb[2] = {__builtin_bit_cast(i16x8, i32x4{(int)pw[0], (int)pw[1], (int)pw[2], (int)pw[3]}),
                              __builtin_bit_cast(i16x8, i32x4{(int)pw[4], (int)pw[5], (int)pw[6], (int)pw[7]})};
-        // ---- O^T += V^T P^T: rolling prefetch of V^T fragments ----
         constexpr int NV = 2 * NT;
-        constexpr int VP = NV < 2 ? NV : 2;
+        constexpr int VP = 2;
         // jh = 0 / 1: keys 16 kb + 4 h + r and 16 kb + 8 + 4 h + r
         auto vaddr = [&](int idx, int jh) {
           const int kb = idx / NT, nb = dg * NT + idx % NT;
@@ -393,72 +517,29 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(
         };
         i16x4 va[VP], vb[VP];
 #pragma unroll
-        for (int j = 0; j < VP; ++j) {
-          va[j] = lds_read_tr(vaddr(j, 0));
-          vb[j] = lds_read_tr(vaddr(j, 1));
+        for (int j2 = 0; j2 < VP; ++j2) {
+          va[j2] = lds_read_tr(vaddr(j2, 0));
+          vb[j2] = lds_read_tr(vaddr(j2, 1));
         }
 #pragma unroll
         for (int idx = 0; idx < NV; ++idx) {
           const int kb = idx / NT, nt = idx % NT;
           i16x4 v0 = va[idx % VP], v1 = vb[idx % VP];
           if (tail) {
-            v0 = zero_from(v0, nvalid - (16 * kb + 4 * h));
-            v1 = zero_from(v1, nvalid - (16 * kb + 8 + 4 * h));
+            v0 = zero_from(v0, nv_lane - 16 * kb);
+            v1 = zero_from(v1, nv_lane - (16 * kb + 8));
           }
+          if (kb == 0 && rescale) acc_scale<OREGS>(o[nt], alpha);
           o[nt] = mfma32(cat(v0, v1), pb[kb], o[nt]);
           if (idx + VP < NV) {
             va[idx % VP] = lds_read_tr(vaddr(idx + VP, 0));
             vb[idx % VP] = lds_read_tr(vaddr(idx + VP, 1));
           }
+          if (first_slot >= 0) fire_slot(first_slot + idx);
           __builtin_amdgcn_sched_barrier(0);
         }
       } else {
-        const int gq = lane >> 4;
-        // ---- scores S^T for two 16-key blocks x 16 rows ----
-        constexpr int KP = 8;
-        i16x8 kf[KP];
-        auto kaddr = [&](int j) {  // j = 2 * ks + key block
-          const int ks = j >> 1, tb2 = j & 1;
-          return st + tb2 * 16 * kRowBytes + koff[ks & 1] + 128 * (ks >> 1);
-        };
-#pragma unroll
-        for (int j = 0; j < KP; ++j) kf[j] = lds_read_b128(kaddr(j));
-        f32x4 sacc[2] = {f32x4{}, f32x4{}};
-#pragma unroll
-        for (int j = 0; j < 2 * KSTEPS; ++j) {
-          sacc[j & 1] = mfma16(kf[j % KP], qf[j >> 1], sacc[j & 1]);
-          if (j + KP < 2 * KSTEPS) kf[j % KP] = lds_read_b128(kaddr(j + KP));
-          __builtin_amdgcn_sched_barrier(0);
-        }
-        // ---- online softmax (lane: row lr, 8 keys) ----
-        float x[8];
-        float mx = -INFINITY;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) x[j] = sacc[j >> 2][j & 3] * a.scale_log2;
-        if (!full) {
-#pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            const int tk = 16 * (j >> 2) + 4 * gq + (j & 3);
-            x[j] = (tk < nvalid && tok0 + tk < row_lim) ? x[j] : -INFINITY;
-          }
-        }
-#pragma unroll
-        for (int j = 0; j < 8; ++j) mx = fmaxf(mx, x[j]);
-        mx = fmaxf(mx, __shfl_xor(mx, 16));
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        if (__any(mx > m_run + kTau)) {
-          const float m_new = fmaxf(m_run, mx);
-          const float alpha = fast_exp2(m_run - m_new);
-          m_run = m_new;
-          l_run *= alpha;
-          lr_run *= alpha;
-#pragma unroll
-          for (int nt = 0; nt < NT; ++nt) acc_scale<kPin, OREGS>(o[nt], alpha);
-        }
-        uint32_t pw[4];
-        weights_bf16<8>(x, m_run, pw, &l_run, &lr_run);
         const i16x8 pb = __builtin_bit_cast(i16x8, i32x4{(int)pw[0], (int)pw[1], (int)pw[2], (int)pw[3]});
-        // ---- O^T += V^T P^T ----
         constexpr int VP = NT < 4 ? NT : 4;
         auto vaddr = [&](int nt) {
           const int nb = dg * NT + nt;
@@ -466,26 +547,145 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(
         };
         i16x4 va[VP], vb[VP];
 #pragma unroll
-        for (int j = 0; j < VP; ++j) {
-          va[j] = lds_read_tr(vaddr(j));
-          vb[j] = lds_read_tr(vaddr(j) + 16 * kRowBytes);
+        for (int j2 = 0; j2 < VP; ++j2) {
+          va[j2] = lds_read_tr(vaddr(j2));
+          vb[j2] = lds_read_tr(vaddr(j2) + 16 * kRowBytes);
         }
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
           i16x4 v0 = va[nt % VP], v1 = vb[nt % VP];
           if (tail) {
-            v0 = zero_from(v0, nvalid - 4 * gq);
-            v1 = zero_from(v1, nvalid - (16 + 4 * gq));
+            v0 = zero_from(v0, nv_lane);
+            v1 = zero_from(v1, nv_lane - 16);
           }
+          if (rescale) acc_scale<OREGS>(o[nt], alpha);
           o[nt] = mfma16(cat(v0, v1), pb, o[nt]);
           if (nt + VP < NT) {
             va[nt % VP] = lds_read_tr(vaddr(nt + VP));
             vb[nt % VP] = lds_read_tr(vaddr(nt + VP) + 16 * kRowBytes);
           }
+          if (first_slot >= 0) fire_slot(first_slot + nt);
           __builtin_amdgcn_sched_barrier(0);
         }
       }
-      }(lds + (cstage & (kSlots - 1)) * kStageBytes, lds + ((cstage + 3) & (kSlots - 1)) * kStageBytes);
+    };
+
+    // Full scores of a stage from the exchange buffer `xb`, which holds every
+    // wave's partial scores; the terms are added in a fixed order (k-share 0
+    // then 1), so the waves of a row group get identical scores.
+    auto gather = [&](const char MLA_LDS* xb, float* sc) {
+      if constexpr (R == 32) {
+        const char MLA_LDS* p0 = xb + (rg * DG + 0) * 4096 + lane * 16;
+        const char MLA_LDS* p1 = xb + (rg * DG + 1) * 4096 + lane * 16;
+#pragma unroll
+        for (int qd = 0; qd < 4; ++qd) {
+          const f32x4 u = lds_read_f4(p0 + qd * 1024), v = lds_read_f4(p1 + qd * 1024);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) sc[4 * qd + e] = u[e] + v[e];
+        }
+      } else if constexpr (KB_W == 2) {
+        const char MLA_LDS* p0 = xb + (rg * DG + 0) * 2048 + lane * 16;
+        const char MLA_LDS* p1 = xb + (rg * DG + 1) * 2048 + lane * 16;
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const f32x4 u = lds_read_f4(p0 + t * 1024), v = lds_read_f4(p1 + t * 1024);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) sc[4 * t + e] = u[e] + v[e];
+        }
+      } else {
+        // DG = 4: wave dg holds key block dg / 2, k-share dg % 2
+        const char MLA_LDS* base = xb + rg * DG * 1024 + lane * 16;
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const f32x4 u = lds_read_f4(base + (2 * t) * 1024), v = lds_read_f4(base + (2 * t + 1) * 1024);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) sc[4 * t + e] = u[e] + v[e];
+        }
+      }
+    };
+
+    if (nst > 0) {
+      for (int jq = 0; jq < NQ; ++jq, ++cstage) {
+        stage_ready();
+        [&](const char MLA_LDS* __restrict__ rd, char MLA_LDS* __restrict__ wr) {
+          plan(wr);
+          fire_all();
+          if (jq == q_stage) {
+            const char MLA_LDS* qs = rd + q_row0 * kRowBytes;
+#pragma unroll
+            for (int ks = 0; ks < KS_W; ++ks) qf[ks] = lds_read_b128(qs + kstep_off(ks));
+          }
+        }(slot_of(cstage), slot_of(cstage + 2));
+      }
+
+      for (int s = 0; s < nst; ++s, ++cstage) {
+        stage_ready();
+        char MLA_LDS* xw = xch0 + (T::XCH_BUFS == 2 ? (s & 1) * T::XCH_ONE : 0);
+        const char MLA_LDS* xr = xch0 + (T::XCH_BUFS == 2 ? ((s + 1) & 1) * T::XCH_ONE : 0);
+        [&](const char MLA_LDS* __restrict__ rd, const char MLA_LDS* __restrict__ prev,
+            char MLA_LDS* __restrict__ wr, char MLA_LDS* __restrict__ xwr,
+            const char MLA_LDS* __restrict__ xrd) {
+          plan(wr);
+          // full scores of the previous stage (its partials were exchanged)
+          float sc[SREGS];
+          if (s > 0) {
+            gather(xrd, sc);
+            if constexpr (T::XCH_BUFS == 1) block_barrier();  // every wave has read them
+          }
+          // partial scores of this stage over this wave's k-steps
+          constexpr int NK = KS_W * KB_W;
+          constexpr int KP = 4;
+          auto kaddr = [&](int i) {
+            if constexpr (R == 32) return rd + kstep_off(i);
+            else {
+              const int kb = KB_W == 2 ? (i & 1) : kbs;
+              return rd + kb * 16 * kRowBytes + kstep_off(i / KB_W);
+            }
+          };
+          i16x8 kf[KP];
+#pragma unroll
+          for (int i = 0; i < KP; ++i) kf[i] = lds_read_b128(kaddr(i));
+          if constexpr (R == 32) {
+            f32x16 sa = {};
+#pragma unroll
+            for (int i = 0; i < NK; ++i) {
+              sa = mfma32(kf[i % KP], qf[i], sa);
+              if (i + KP < NK) kf[i % KP] = lds_read_b128(kaddr(i + KP));
+              fire_slot(i);
+              __builtin_amdgcn_sched_barrier(0);
+            }
+#pragma unroll
+            for (int qd = 0; qd < 4; ++qd)
+              lds_write_f4(xwr + w * 4096 + qd * 1024 + lane * 16,
+                           f32x4{sa[4 * qd], sa[4 * qd + 1], sa[4 * qd + 2], sa[4 * qd + 3]});
+            if (s > 0) finish(sc, s - 1, prev, T::QK_MFMA);
+            else fire_from(T::QK_MFMA);
+          } else {
+            f32x4 sacc[KB_W];
+#pragma unroll
+            for (int t = 0; t < KB_W; ++t) sacc[t] = f32x4{};
+#pragma unroll
+            for (int i = 0; i < NK; ++i) {
+              sacc[i % KB_W] = mfma16(kf[i % KP], qf[i / KB_W], sacc[i % KB_W]);
+              if (i + KP < NK) kf[i % KP] = lds_read_b128(kaddr(i + KP));
+              fire_slot(i);
+              __builtin_amdgcn_sched_barrier(0);
+            }
+#pragma unroll
+            for (int t = 0; t < KB_W; ++t) lds_write_f4(xwr + (w * KB_W + t) * 1024 + lane * 16, sacc[t]);
+            if (s > 0) finish(sc, s - 1, prev, T::QK_MFMA);
+            else fire_from(T::QK_MFMA);
+          }
+        }(slot_of(cstage), slot_of(cstage - 1), slot_of(cstage + 2), xw, xr);
+      }
+      // drain: the last stage's partials are exchanged; finish it
+      block_barrier();
+      {
+        const char MLA_LDS* xr = xch0 + (T::XCH_BUFS == 2 ? ((nst - 1) & 1) * T::XCH_ONE : 0);
+        float sc[SREGS];
+        gather(xr, sc);
+        finish(sc, nst - 1, slot_of(cstage - 1), -1);
+      }
     }
 
     // ---- epilogue: normalise and write this piece --------------------------
@@ -504,7 +704,7 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(
     const float lse_row = empty ? -INFINITY : (m_run + fast_log2(lt)) * kLn2;
     if (my_row < M) {
       const long long out_row = ((long long)b * a.s_q + q_t) * a.h_q + q_h;
-      const long long part_row = ((long long)(s0 + split_k) * a.h_kv + g) * M + my_row;
+      const long long part_row = ((long long)slot * a.h_kv + g) * M + my_row;
       const bool lse_writer = dg == 0 && lane < R;
       // dims held by this lane: 4 consecutive dims per group of 4 accumulators
       auto dim_of = [&](int nt, int qd) {
@@ -512,7 +712,7 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(
         return R == 32 ? 32 * nb + 8 * qd + 4 * (lane >> 5) : 16 * nb + 4 * (lane >> 4);
       };
       constexpr int QUADS = OREGS / 4;
-      if (nsplit == 1) {
+      if (whole) {
         if (lse_writer) lse[out_row] = lse_row;
         uint16_t* orow = out + out_row * kValueDim;
 #pragma unroll
@@ -520,8 +720,8 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(
 #pragma unroll
           for (int qd = 0; qd < QUADS; ++qd) {
             uint2 pk;
-            pk.x = pack_bf16(acc_read<kPin>(o[nt][4 * qd + 0]) * inv, acc_read<kPin>(o[nt][4 * qd + 1]) * inv);
-            pk.y = pack_bf16(acc_read<kPin>(o[nt][4 * qd + 2]) * inv, acc_read<kPin>(o[nt][4 * qd + 3]) * inv);
+            pk.x = pack_bf16((o[nt][4 * qd + 0]) * inv, (o[nt][4 * qd + 1]) * inv);
+            pk.y = pack_bf16((o[nt][4 * qd + 2]) * inv, (o[nt][4 * qd + 3]) * inv);
             *reinterpret_cast<uint2*>(orow + dim_of(nt, qd)) = pk;
           }
         }
@@ -533,42 +733,49 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(
 #pragma unroll
           for (int qd = 0; qd < QUADS; ++qd) {
             *reinterpret_cast<float4*>(prow + dim_of(nt, qd)) =
-                make_float4(acc_read<kPin>(o[nt][4 * qd + 0]) * inv, acc_read<kPin>(o[nt][4 * qd + 1]) * inv,
-                            acc_read<kPin>(o[nt][4 * qd + 2]) * inv, acc_read<kPin>(o[nt][4 * qd + 3]) * inv);
+                make_float4((o[nt][4 * qd + 0]) * inv, (o[nt][4 * qd + 1]) * inv,
+                            (o[nt][4 * qd + 2]) * inv, (o[nt][4 * qd + 3]) * inv);
           }
         }
       }
     }
   }
+  // Out-of-range loads past the end of the stream may still be in flight:
+  // they must land before the workgroup's LDS is released.
+  wait_vmcnt<0>();
 }
 
 #define MLA_DECODE_PARAMS                                                                   \
   const uint16_t* __restrict__, const uint16_t* __restrict__, const int32_t* __restrict__,  \
-      const int32_t* __restrict__, const int32_t* __restrict__, const int32_t* __restrict__, \
-      uint16_t* __restrict__, float* __restrict__, float* __restrict__, float* __restrict__, \
-      DecodeArgs
-template __global__ void decode_kernel<16, 1, 4>(MLA_DECODE_PARAMS);
-template __global__ void decode_kernel<16, 2, 2>(MLA_DECODE_PARAMS);
-template __global__ void decode_kernel<32, 2, 2>(MLA_DECODE_PARAMS);
-template __global__ void decode_kernel<32, 4, 1>(MLA_DECODE_PARAMS);
+      const int32_t* __restrict__, const int32_t* __restrict__, uint16_t* __restrict__,      \
+      float* __restrict__, float* __restrict__, float* __restrict__, DecodeArgs
+template __global__ void decode_kernel<16, 1, 4, false>(MLA_DECODE_PARAMS);
+template __global__ void decode_kernel<16, 2, 2, false>(MLA_DECODE_PARAMS);
+template __global__ void decode_kernel<32, 2, 2, false>(MLA_DECODE_PARAMS);
+template __global__ void decode_kernel<16, 1, 4, true>(MLA_DECODE_PARAMS);
+template __global__ void decode_kernel<16, 2, 2, true>(MLA_DECODE_PARAMS);
+template __global__ void decode_kernel<32, 2, 2, true>(MLA_DECODE_PARAMS);
 
-template <int R, int RG, int DG>
+template <int R, int RG, int DG, bool QG>
 static hipError_t launch_t(const DecodeArgs& a, hipStream_t stream) {
   const int grid = a.num_parts * a.m_tiles * a.h_kv;
-  hipLaunchKernelGGL((decode_kernel<R, RG, DG>), dim3(grid), dim3(256), 0, stream, a.q, a.kv,
-                     a.block_table, a.seqlens, a.meta, a.num_splits, a.out, a.lse, a.o_part,
-                     a.lse_part, a);
+  hipLaunchKernelGGL((decode_kernel<R, RG, DG, QG>), dim3(grid), dim3(256), 0, stream, a.q, a.kv,
+                     a.block_table, a.seqlens, a.meta, a.out, a.lse, a.o_part, a.lse_part, a);
   return hipGetLastError();
 }
 
-hipError_t launch_decode(const DecodeArgs& a, int tile_rows, hipStream_t stream) {
+template <bool QG>
+static hipError_t launch_q(const DecodeArgs& a, int tile_rows, hipStream_t stream) {
   switch (tile_rows) {
-    case 16: return launch_t<16, 1, 4>(a, stream);
-    case 32: return launch_t<16, 2, 2>(a, stream);
-    case 64: return launch_t<32, 2, 2>(a, stream);
-    case 128: return launch_t<32, 4, 1>(a, stream);
+    case 16: return launch_t<16, 1, 4, QG>(a, stream);
+    case 32: return launch_t<16, 2, 2, QG>(a, stream);
+    case 64: return launch_t<32, 2, 2, QG>(a, stream);
     default: return hipErrorInvalidValue;
   }
+}
+
+hipError_t launch_decode(const DecodeArgs& a, int tile_rows, hipStream_t stream) {
+  return a.h_kv == 1 ? launch_q<false>(a, tile_rows, stream) : launch_q<true>(a, tile_rows, stream);
 }
 
 }  // namespace mla

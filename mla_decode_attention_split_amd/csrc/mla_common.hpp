@@ -72,9 +72,15 @@ __device__ __forceinline__ float bf16_hi(uint32_t p) { return __uint_as_float(p 
 // Uniform read of read-only metadata through the scalar cache, waited on in
 // the same asm block.  Used inside the stage loop, where the compiler would
 // otherwise emit a vector load whose wait drains the staged key loads.
+// The address must be uniform; it is passed through readfirstlane so that it
+// is held in scalar registers whatever the surrounding code does with it.
 __device__ __forceinline__ int sload_i32(const int32_t* p) {
+  const uint64_t a = reinterpret_cast<uint64_t>(p);
+  const uint64_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  const uint64_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32));
+  const int32_t* ps = reinterpret_cast<const int32_t*>((hi << 32) | lo);
   int v;
-  asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(p) : "memory");
+  asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(ps) : "memory");
   return v;
 }
 

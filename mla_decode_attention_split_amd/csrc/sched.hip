@@ -67,7 +67,10 @@ __global__ __launch_bounds__(NT) void sched_kernel(const int32_t* __restrict__ s
   constexpr bool kSlInLds = MAXB <= 4096;
   __shared__ long long C[MAXB + 1];  // C[b] = cost of the sequences before b
   __shared__ int SL_lds[kSlInLds ? MAXB : 1];
+  __shared__ int NS_lds[kSlInLds ? MAXB + 1 : 1];
   auto SL = [&](int b) -> int { return kSlInLds ? SL_lds[b] : seqlens[b]; };
+  // num_splits as written by this kernel (read back only after the barrier)
+  auto NS = [&](int b) -> int { return kSlInLds ? NS_lds[b] : num_splits[b]; };
   __shared__ long long scratch[NT / 64];
   const int tid = threadIdx.x;
   const int per = (batch + NT - 1) / NT;
@@ -109,6 +112,7 @@ __global__ __launch_bounds__(NT) void sched_kernel(const int32_t* __restrict__ s
     const int b = b0 + i;
     if (b < batch) {
       num_splits[b] = (int32_t)pbase;
+      if constexpr (kSlInLds) NS_lds[b] = (int32_t)pbase;
       const long long cb = C[b];
       const long long u = units_of(SL(b));
       const long long first = u > 0 ? (cb + fc) / T : (cb + fc - 1) / T;
@@ -116,8 +120,12 @@ __global__ __launch_bounds__(NT) void sched_kernel(const int32_t* __restrict__ s
       pbase += last - first + 1;
     }
   }
-  if (tid == 0) num_splits[batch] = (int32_t)ptotal;
-  __syncthreads();  // C complete
+  if (tid == 0) {
+    num_splits[batch] = (int32_t)ptotal;
+    if constexpr (kSlInLds) NS_lds[batch] = (int32_t)ptotal;
+  }
+  __threadfence_block();
+  __syncthreads();  // C and num_splits complete
 
   // Cost positions that decide a sequence's first and last part:
   //   last part  = floor(KL_b / T), KL_b = C_{b+1} - 1
@@ -161,7 +169,9 @@ __global__ __launch_bounds__(NT) void sched_kernel(const int32_t* __restrict__ s
       long long tok_end = u_end * kStage;
       if (tok_end > SL(be)) tok_end = SL(be);
       w0 = i32x4{bb, (int32_t)(u_begin * kStage), be, (int32_t)tok_end};
-      w1.x = (int32_t)(p - KF(bb) / T);  // split index of this piece within sequence bb
+      // partial slot of bb's piece (num_splits[bb] + its split index), both
+      // sequence lengths, and the partial slot of be's piece (split 0)
+      w1 = i32x4{NS(bb) + (int32_t)(p - KF(bb) / T), SL(bb), SL(be), NS(be)};
     }
     i32x4* dst = reinterpret_cast<i32x4*>(meta + (long long)p * kMetaWords);
     dst[0] = w0;

@@ -347,7 +347,10 @@ int mla_oracle_schedule(const int32_t *seqlens, int B, int unit_tokens, int num_
     w[1] = (int32_t)(u_begin * unit_tokens);
     w[2] = be;
     w[3] = (int32_t)tok_end;
-    w[4] = (int32_t)(p - first[bb]);
+    w[4] = num_splits[bb] + (int32_t)(p - first[bb]); /* partial slot of the first piece */
+    w[5] = seqlens[bb];
+    w[6] = seqlens[be];
+    w[7] = num_splits[be]; /* partial slot of the last piece (its first split) */
   }
   free(C);
   free(first);

@@ -348,12 +348,16 @@ def enumerate_parts(seqlens, num_parts, fixed_cost, unit):
     return units, where, T
 
 
-def pieces_from_meta(meta, seqlens):
+def pieces_from_meta(meta, seqlens, ns):
     """Expand tile metadata into {(b, split): (part, key_lo, key_hi)}."""
     got = {}
     for p, w in enumerate(meta):
-        bb, kb, be, ke, k0 = (int(x) for x in w[:5])
-        assert (w[5:] == 0).all()
+        bb, kb, be, ke, slot0, n_first, n_last, slot_last = (int(x) for x in w)
+        if bb > be:
+            assert (bb, kb, be, ke) == (0, 0, -1, 0) and (w[4:] == 0).all()
+            continue
+        k0 = slot0 - int(ns[bb])
+        assert n_first == seqlens[bb] and n_last == seqlens[be] and slot_last == ns[be]
         for b in range(bb, be + 1):
             lo = kb if b == bb else 0
             hi = ke if b == be else int(seqlens[b])
@@ -375,7 +379,7 @@ def test_schedule_matches_unit_enumeration(seed):
     unit = int(rng.choice([16, 32, 64]))
     meta, ns = oracle.schedule(lens, num_parts=num_parts, fixed_cost=fixed_cost, unit_tokens=unit)
     units, where, T = enumerate_parts(lens, num_parts, fixed_cost, unit)
-    got = pieces_from_meta(meta, lens)
+    got = pieces_from_meta(meta, lens, ns)
     assert ns[0] == 0
     for b in range(B):
         parts = sorted(set(where[b]))
