@@ -113,25 +113,6 @@ __device__ __forceinline__ i16x4 zero_from(i16x4 v, int first_bad) {
   return r;
 }
 
-// exp2 of K masked scores -> packed bf16 B operand.  Adds the fp32 weights to
-// *l (the softmax denominator behind lse) and the bf16-rounded weights to *lr
-// (the normaliser of out).
-template <int K>
-__device__ __forceinline__ void weights_bf16(const float* x, float m, uint32_t* packed, float* l,
-                                             float* lr) {
-  float sum = 0.f, rsum = 0.f;
-#pragma unroll
-  for (int i = 0; i < K; i += 2) {
-    const float p0 = fast_exp2(x[i] - m), p1 = fast_exp2(x[i + 1] - m);
-    const uint32_t p = pack_bf16(p0, p1);
-    packed[i >> 1] = p;
-    sum += p0 + p1;
-    rsum += bf16_lo(p) + bf16_hi(p);
-  }
-  *l += sum;
-  *lr += rsum;
-}
-
 // Wave-wide exclusive prefix sum of an int.
 __device__ __forceinline__ int wave_exclusive_sum(int v, int lane) {
   int x = v;
@@ -193,7 +174,7 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(
   char MLA_LDS* xch0 = lds + kLdsBytes;
 
   const int tid = threadIdx.x;
-  const int w = tid >> 6;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int lane = tid & 63;
   const int rg = w / DG;
   const int dg = w % DG;
@@ -470,100 +451,130 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(
     float m_run = kMinit, l_run = 0.f, lr_run = 0.f;
     i16x8 qf[KS_W];
 
-    // Finish key stage sp of this piece (ring slot `st`): softmax of the full
-    // scores sc and O^T += V^T P^T.  Loads for the stage in flight are fired
-    // at issue points first_slot.. of the stage's schedule.
-    auto finish = [&](const float* sc, int sp, const char MLA_LDS* st, int first_slot) {
+    // Mask the scores of key stage sp (keys past the end, or past the row's
+    // causal limit) and scale them to the log2 domain.
+    auto prep = [&](float* x, int sp) {
       const int tok0 = lo + sp * kStage;
       const int nvalid = N - tok0 < kStage ? N - tok0 : kStage;
-      const bool tail = nvalid < kStage;
       const bool full = tok0 + kStage <= lim_all;  // no key of the stage is masked
-      float x[SREGS];
 #pragma unroll
-      for (int i = 0; i < SREGS; ++i) x[i] = sc[i] * a.scale_log2;
+      for (int i = 0; i < SREGS; ++i) x[i] *= a.scale_log2;
       if (!full) {
         const int lim = ((row_lim - tok0 < nvalid) ? row_lim - tok0 : nvalid) - key_lane;
 #pragma unroll
         for (int i = 0; i < SREGS; ++i) x[i] = key_reg(i) < lim ? x[i] : -INFINITY;
       }
-      float mx = x[0];
-#pragma unroll
-      for (int i = 1; i < SREGS; ++i) mx = fmaxf(mx, x[i]);
-      if constexpr (R == 16) mx = max_xor16(mx);
-      mx = max_xor32(mx);
-      // Raise the running max only when some row's max exceeds it by more
-      // than kTau; O is then rescaled tile by tile just before its next MFMA.
-      const bool rescale = __any(mx > m_run + kTau);
-      float alpha = 1.f;
-      if (rescale) {
-        const float m_new = fmaxf(m_run, mx);
-        alpha = fast_exp2(m_run - m_new);
-        m_run = m_new;
-        l_run *= alpha;
-        lr_run *= alpha;
-      }
+    };
+    // Online softmax of one stage's scores x, cut into slices so that it can
+    // be interleaved with the next stage's score MFMAs (the slices have no
+    // branches).  The running max is raised only when some row's max exceeds
+    // it by more than kTau; alpha is then the factor O must be scaled by
+    // (1 otherwise).
+    constexpr int kExpSlices = SREGS / 4;
+    constexpr int kSoftSlices = 3 + kExpSlices;
+    struct SoftState {
+      float mx, alpha, sum, rsum;
+      bool rescale;
       uint32_t pw[SREGS / 2];
-      weights_bf16<SREGS>(x, m_run, pw, &l_run, &lr_run);
+    };
+    auto soft_slice = [&](const float* x, SoftState& st, int slice) {
+      if (slice == 0) {
+        float mx = x[0];
+#pragma unroll
+        for (int i = 1; i < SREGS; ++i) mx = fmaxf(mx, x[i]);
+        st.mx = mx;
+      } else if (slice == 1) {
+        if constexpr (R == 16) st.mx = max_xor16(st.mx);
+        st.mx = max_xor32(st.mx);
+      } else if (slice == 2) {
+        const bool rs = __any(st.mx > m_run + kTau);
+        const float m_new = fmaxf(m_run, st.mx);
+        const float al = rs ? fast_exp2(m_run - m_new) : 1.f;
+        m_run = rs ? m_new : m_run;
+        l_run *= al;
+        lr_run *= al;
+        st.rescale = rs;
+        st.alpha = al;
+        st.sum = 0.f;
+        st.rsum = 0.f;
+      } else if (slice < kSoftSlices) {
+        const int e0 = 4 * (slice - 3);
+        const bf16x2 ones = __builtin_bit_cast(bf16x2, 0x3f803f80u);
+#pragma unroll
+        for (int i = 0; i < 4; i += 2) {
+          const float p0 = fast_exp2(x[e0 + i] - m_run), p1 = fast_exp2(x[e0 + i + 1] - m_run);
+          const uint32_t pk = pack_bf16(p0, p1);
+          st.pw[(e0 + i) >> 1] = pk;
+          st.sum += p0 + p1;
+          st.rsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk), ones, st.rsum, false);
+        }
+        if (slice == kSoftSlices - 1) {
+          l_run += st.sum;
+          lr_run += st.rsum;
+        }
+      }
+    };
+    // O^T += V^T P^T for key stage sp held in ring slot `st`; loads of the
+    // stage in flight are fired at issue points first_slot.. (none if < 0).
+    auto pv = [&](const uint32_t* pw, bool rescale, float alpha, int sp, const char MLA_LDS* st,
+                  int first_slot) {
+      const int tok0 = lo + sp * kStage;
+      const int nvalid = N - tok0 < kStage ? N - tok0 : kStage;
+      const bool tail = nvalid < kStage;
       const int nv_lane = nvalid - key_lane;  // valid keys past this lane's first key
       if constexpr (R == 32) {
         const i16x8 pb[2] = {__builtin_bit_cast(i16x8, i32x4{(int)pw[0], (int)pw[1], (int)pw[2], (int)pw[3]}),
                              __builtin_bit_cast(i16x8, i32x4{(int)pw[4], (int)pw[5], (int)pw[6], (int)pw[7]})};
         constexpr int NV = 2 * NT;
         constexpr int VP = 2;
-        // jh = 0 / 1: keys 16 kb + 4 h + r and 16 kb + 8 + 4 h + r
-        auto vaddr = [&](int idx, int jh) {
+        // keys 16 kb + 4 h + r (low half) and 16 kb + 8 + 4 h + r (high half)
+        auto vread = [&](int idx) {
           const int kb = idx / NT, nb = dg * NT + idx % NT;
-          return st + voff[2 * (nb & 1) + jh] + 128 * (nb >> 1) + (16 * kb + 8 * jh) * kRowBytes;
+          const char MLA_LDS* p = st + 128 * (nb >> 1) + 16 * kb * kRowBytes;
+          const i16x4 v0 = lds_read_tr(p + voff[2 * (nb & 1)]);
+          const i16x4 v1 = lds_read_tr(p + voff[2 * (nb & 1) + 1] + 8 * kRowBytes);
+          return cat(v0, v1);
         };
-        i16x4 va[VP], vb[VP];
+        i16x8 va[VP];
 #pragma unroll
-        for (int j2 = 0; j2 < VP; ++j2) {
-          va[j2] = lds_read_tr(vaddr(j2, 0));
-          vb[j2] = lds_read_tr(vaddr(j2, 1));
-        }
+        for (int j2 = 0; j2 < VP; ++j2) va[j2] = vread(j2);
 #pragma unroll
         for (int idx = 0; idx < NV; ++idx) {
           const int kb = idx / NT, nt = idx % NT;
-          i16x4 v0 = va[idx % VP], v1 = vb[idx % VP];
+          i16x8 v = va[idx % VP];
           if (tail) {
-            v0 = zero_from(v0, nv_lane - 16 * kb);
-            v1 = zero_from(v1, nv_lane - (16 * kb + 8));
+            const i16x4 v0 = zero_from(i16x4{v[0], v[1], v[2], v[3]}, nv_lane - 16 * kb);
+            const i16x4 v1 = zero_from(i16x4{v[4], v[5], v[6], v[7]}, nv_lane - (16 * kb + 8));
+            v = cat(v0, v1);
           }
           if (kb == 0 && rescale) acc_scale<OREGS>(o[nt], alpha);
-          o[nt] = mfma32(cat(v0, v1), pb[kb], o[nt]);
-          if (idx + VP < NV) {
-            va[idx % VP] = lds_read_tr(vaddr(idx + VP, 0));
-            vb[idx % VP] = lds_read_tr(vaddr(idx + VP, 1));
-          }
+          o[nt] = mfma32(v, pb[kb], o[nt]);
+          if (idx + VP < NV) va[idx % VP] = vread(idx + VP);
           if (first_slot >= 0) fire_slot(first_slot + idx);
           __builtin_amdgcn_sched_barrier(0);
         }
       } else {
         const i16x8 pb = __builtin_bit_cast(i16x8, i32x4{(int)pw[0], (int)pw[1], (int)pw[2], (int)pw[3]});
         constexpr int VP = NT < 4 ? NT : 4;
-        auto vaddr = [&](int nt) {
+        auto vread = [&](int nt) {
           const int nb = dg * NT + nt;
-          return st + voff[nb & 3] + 128 * (nb >> 2);
+          const char MLA_LDS* p = st + voff[nb & 3] + 128 * (nb >> 2);
+          return cat(lds_read_tr(p), lds_read_tr(p + 16 * kRowBytes));
         };
-        i16x4 va[VP], vb[VP];
+        i16x8 va[VP];
 #pragma unroll
-        for (int j2 = 0; j2 < VP; ++j2) {
-          va[j2] = lds_read_tr(vaddr(j2));
-          vb[j2] = lds_read_tr(vaddr(j2) + 16 * kRowBytes);
-        }
+        for (int j2 = 0; j2 < VP; ++j2) va[j2] = vread(j2);
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
-          i16x4 v0 = va[nt % VP], v1 = vb[nt % VP];
+          i16x8 v = va[nt % VP];
           if (tail) {
-            v0 = zero_from(v0, nv_lane);
-            v1 = zero_from(v1, nv_lane - 16);
+            const i16x4 v0 = zero_from(i16x4{v[0], v[1], v[2], v[3]}, nv_lane);
+            const i16x4 v1 = zero_from(i16x4{v[4], v[5], v[6], v[7]}, nv_lane - 16);
+            v = cat(v0, v1);
           }
           if (rescale) acc_scale<OREGS>(o[nt], alpha);
-          o[nt] = mfma16(cat(v0, v1), pb, o[nt]);
-          if (nt + VP < NT) {
-            va[nt % VP] = lds_read_tr(vaddr(nt + VP));
-            vb[nt % VP] = lds_read_tr(vaddr(nt + VP) + 16 * kRowBytes);
-          }
+          o[nt] = mfma16(v, pb, o[nt]);
+          if (nt + VP < NT) va[nt % VP] = vread(nt + VP);
           if (first_slot >= 0) fire_slot(first_slot + nt);
           __builtin_amdgcn_sched_barrier(0);
         }
@@ -604,6 +615,69 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(
       }
     };
 
+    // One iteration of the key-stage pipeline.  HP: finish the previous stage
+    // sp = s - 1 (its partial scores are in xrd, its keys in ring slot prev);
+    // HC: compute this wave's partial scores of stage s (ring slot rd) into
+    // xwr.  The score MFMAs of stage s and the softmax of stage s - 1 are
+    // independent and are scheduled into one region.
+    auto kv_step = [&](auto hp, auto hc, const char MLA_LDS* __restrict__ rd,
+                       const char MLA_LDS* __restrict__ prev, char MLA_LDS* __restrict__ xwr,
+                       const char MLA_LDS* __restrict__ xrd, int s) {
+      constexpr bool HP = decltype(hp)::value, HC = decltype(hc)::value;
+      float x[SREGS];
+      if constexpr (HP) {
+        gather(xrd, x);
+        if constexpr (T::XCH_BUFS == 1 && HC) block_barrier();  // every wave has read them
+        prep(x, s - 1);
+      }
+      constexpr int NK = KS_W * KB_W;
+      constexpr int KP = 4;
+      auto kaddr = [&](int i) {
+        if constexpr (R == 32) return rd + kstep_off(i);
+        else {
+          const int kb = KB_W == 2 ? (i & 1) : kbs;
+          return rd + kb * 16 * kRowBytes + kstep_off(i / KB_W);
+        }
+      };
+      using SAcc = typename std::conditional<R == 32, f32x16, f32x4>::type;
+      SAcc sacc[R == 32 ? 1 : KB_W];
+      SoftState ss;
+      if constexpr (HC) {
+        static_assert(NK >= kSoftSlices, "softmax slices fit between the score MFMAs");
+        i16x8 kf[KP];
+#pragma unroll
+        for (int i = 0; i < KP; ++i) kf[i] = lds_read_b128(kaddr(i));
+#pragma unroll
+        for (int t = 0; t < (R == 32 ? 1 : KB_W); ++t) sacc[t] = SAcc{};
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < NK; ++i) {
+          if constexpr (R == 32) sacc[0] = mfma32(kf[i % KP], qf[i], sacc[0]);
+          else sacc[i % KB_W] = mfma16(kf[i % KP], qf[i / KB_W], sacc[i % KB_W]);
+          if (i + KP < NK) kf[i % KP] = lds_read_b128(kaddr(i + KP));
+          fire_slot(i);
+          if constexpr (HP) soft_slice(x, ss, i);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < kSoftSlices; ++i) soft_slice(x, ss, i);
+      }
+      if constexpr (HC) {
+        if constexpr (R == 32) {
+#pragma unroll
+          for (int qd = 0; qd < 4; ++qd)
+            lds_write_f4(xwr + w * 4096 + qd * 1024 + lane * 16,
+                         f32x4{sacc[0][4 * qd], sacc[0][4 * qd + 1], sacc[0][4 * qd + 2], sacc[0][4 * qd + 3]});
+        } else {
+#pragma unroll
+          for (int t = 0; t < KB_W; ++t) lds_write_f4(xwr + (w * KB_W + t) * 1024 + lane * 16, sacc[t]);
+        }
+      }
+      if constexpr (HP) pv(ss.pw, ss.rescale, ss.alpha, s - 1, prev, HC ? T::QK_MFMA : -1);
+      else fire_from(T::QK_MFMA);
+    };
+
     if (nst > 0) {
       for (int jq = 0; jq < NQ; ++jq, ++cstage) {
         stage_ready();
@@ -617,75 +691,24 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(
           }
         }(slot_of(cstage), slot_of(cstage + 2));
       }
-
-      for (int s = 0; s < nst; ++s, ++cstage) {
+      using F = std::false_type;
+      using Tr = std::true_type;
+      // stage 0: scores only
+      stage_ready();
+      plan(slot_of(cstage + 2));
+      kv_step(F{}, Tr{}, slot_of(cstage), slot_of(cstage - 1), xch0, xch0, 0);
+      ++cstage;
+      for (int s = 1; s < nst; ++s, ++cstage) {
         stage_ready();
+        plan(slot_of(cstage + 2));
         char MLA_LDS* xw = xch0 + (T::XCH_BUFS == 2 ? (s & 1) * T::XCH_ONE : 0);
         const char MLA_LDS* xr = xch0 + (T::XCH_BUFS == 2 ? ((s + 1) & 1) * T::XCH_ONE : 0);
-        [&](const char MLA_LDS* __restrict__ rd, const char MLA_LDS* __restrict__ prev,
-            char MLA_LDS* __restrict__ wr, char MLA_LDS* __restrict__ xwr,
-            const char MLA_LDS* __restrict__ xrd) {
-          plan(wr);
-          // full scores of the previous stage (its partials were exchanged)
-          float sc[SREGS];
-          if (s > 0) {
-            gather(xrd, sc);
-            if constexpr (T::XCH_BUFS == 1) block_barrier();  // every wave has read them
-          }
-          // partial scores of this stage over this wave's k-steps
-          constexpr int NK = KS_W * KB_W;
-          constexpr int KP = 4;
-          auto kaddr = [&](int i) {
-            if constexpr (R == 32) return rd + kstep_off(i);
-            else {
-              const int kb = KB_W == 2 ? (i & 1) : kbs;
-              return rd + kb * 16 * kRowBytes + kstep_off(i / KB_W);
-            }
-          };
-          i16x8 kf[KP];
-#pragma unroll
-          for (int i = 0; i < KP; ++i) kf[i] = lds_read_b128(kaddr(i));
-          if constexpr (R == 32) {
-            f32x16 sa = {};
-#pragma unroll
-            for (int i = 0; i < NK; ++i) {
-              sa = mfma32(kf[i % KP], qf[i], sa);
-              if (i + KP < NK) kf[i % KP] = lds_read_b128(kaddr(i + KP));
-              fire_slot(i);
-              __builtin_amdgcn_sched_barrier(0);
-            }
-#pragma unroll
-            for (int qd = 0; qd < 4; ++qd)
-              lds_write_f4(xwr + w * 4096 + qd * 1024 + lane * 16,
-                           f32x4{sa[4 * qd], sa[4 * qd + 1], sa[4 * qd + 2], sa[4 * qd + 3]});
-            if (s > 0) finish(sc, s - 1, prev, T::QK_MFMA);
-            else fire_from(T::QK_MFMA);
-          } else {
-            f32x4 sacc[KB_W];
-#pragma unroll
-            for (int t = 0; t < KB_W; ++t) sacc[t] = f32x4{};
-#pragma unroll
-            for (int i = 0; i < NK; ++i) {
-              sacc[i % KB_W] = mfma16(kf[i % KP], qf[i / KB_W], sacc[i % KB_W]);
-              if (i + KP < NK) kf[i % KP] = lds_read_b128(kaddr(i + KP));
-              fire_slot(i);
-              __builtin_amdgcn_sched_barrier(0);
-            }
-#pragma unroll
-            for (int t = 0; t < KB_W; ++t) lds_write_f4(xwr + (w * KB_W + t) * 1024 + lane * 16, sacc[t]);
-            if (s > 0) finish(sc, s - 1, prev, T::QK_MFMA);
-            else fire_from(T::QK_MFMA);
-          }
-        }(slot_of(cstage), slot_of(cstage - 1), slot_of(cstage + 2), xw, xr);
+        kv_step(Tr{}, Tr{}, slot_of(cstage), slot_of(cstage - 1), xw, xr, s);
       }
       // drain: the last stage's partials are exchanged; finish it
       block_barrier();
-      {
-        const char MLA_LDS* xr = xch0 + (T::XCH_BUFS == 2 ? ((nst - 1) & 1) * T::XCH_ONE : 0);
-        float sc[SREGS];
-        gather(xr, sc);
-        finish(sc, nst - 1, slot_of(cstage - 1), -1);
-      }
+      const char MLA_LDS* xr = xch0 + (T::XCH_BUFS == 2 ? ((nst - 1) & 1) * T::XCH_ONE : 0);
+      kv_step(Tr{}, F{}, slot_of(cstage), slot_of(cstage - 1), nullptr, xr, nst);
     }
 
     // ---- epilogue: normalise and write this piece --------------------------
