@@ -50,6 +50,18 @@ namespace mla {
 constexpr float kTau = 8.0f;        // lazy-rescale threshold (log2 units)
 constexpr float kMinit = -1.0e30f;  // finite "minus infinity" for the running max
 constexpr float kLn2 = 0.69314718055994530942f;
+#ifndef MLA_VP32
+#define MLA_VP32 2
+#endif
+#ifndef MLA_VP16
+#define MLA_VP16 4
+#endif
+#ifndef MLA_KP32
+#define MLA_KP32 4
+#endif
+#ifndef MLA_KP16
+#define MLA_KP16 4
+#endif
 constexpr int kListPages = 128;     // page indices held in registers (2 per lane)
 constexpr int kListPieces = 64;     // sequence lengths held in registers (1 per lane)
 constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, 32-bit data format
@@ -104,13 +116,6 @@ __device__ __forceinline__ void acc_scale(V& o, float s) {
 
 __device__ __forceinline__ i16x8 cat(i16x4 a, i16x4 b) {
   return i16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
-}
-// Zero the elements e >= first_bad of a 4-key fragment (keys past the end).
-__device__ __forceinline__ i16x4 zero_from(i16x4 v, int first_bad) {
-  i16x4 r;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) r[e] = e < first_bad ? v[e] : (short)0;
-  return r;
 }
 
 // Wave-wide exclusive prefix sum of an int.
@@ -321,7 +326,10 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(
   // swizzled row layout as the keys), then the piece's key stages.  Stream
   // position c uses ring slot c % 4; position c + 2 is loaded while position c
   // is computed.  Past the end of the stream the loads are out of range.
-  int lj = 0, lq = 0, ltok = tb, lhi = (bb == be) ? te : n_first, lpg = 0;
+  // Cursor of the stream: piece lj, query stage lq, key token ltok (end lhi),
+  // and the next key stage's page-list position lpos and page half lhalf.
+  int lj = 0, lq = 0, ltok = tb, lhi = (bb == be) ? te : n_first;
+  int lpos = 0, lhalf = (tb >> 5) & 1;
   bool lvalid = true;
   auto next_piece = [&]() {
     while (true) {
@@ -329,8 +337,8 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(
         lvalid = false;
         return;
       }
-      const int lo_cur = lj == 0 ? tb : 0;  // step over the pages of the piece left
-      if (lhi > lo_cur) lpg += (lhi + kPage - 1) / kPage - lo_cur / kPage;
+      lpos += lhalf;  // a piece that ended mid-page: the next page is the next piece's
+      lhalf = 0;
       ++lj;
       lq = 0;
       ltok = 0;
@@ -338,7 +346,10 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(
       if (ltok < lhi) return;
     }
   };
-  if (ltok >= lhi) next_piece();
+  if (ltok >= lhi) {  // the first piece is empty: no page of it is listed
+    lhalf = 0;
+    next_piece();
+  }
 
   // The stream position being loaded: a buffer over its bytes (range 0 =
   // nothing, past the end of the stream) and per-lane offsets (the key-row
@@ -374,10 +385,25 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(
   };
   // Plan the next stream position into ring slot `wr`; the caller fires its
   // LPW loads.
+  const long long page_bytes = (long long)kPage * row_stride;
+  const int half_bytes = kStage * row_stride;
   auto plan = [&](char MLA_LDS* __restrict__ wr) {
     pend_dst = wr + w * 1024;
     pend_q = false;
-    if (lvalid && lq < NQ) {
+    if (lvalid && lq >= NQ) {
+      int page;
+      if (use_list) page = readlane(lpos < 64 ? v_page[0] : v_page[1], lpos & 63);
+      else page = sload_i32(block_table + (long long)(bb + lj) * a.max_blocks + (ltok >> 6));
+      // Rows past the end of the sequence are out of the buffer's range, so
+      // they arrive as zeros: their V rows then contribute exactly nothing
+      // (cache memory past the end may hold anything, NaN included).
+      const int rows = lhi - ltok < kStage ? lhi - ltok : kStage;
+      pend = make_rsrc(kv_bytes + page * page_bytes + lhalf * half_bytes, rows * row_stride);
+      lpos += lhalf;
+      lhalf ^= 1;
+      ltok += kStage;
+      if (ltok >= lhi) next_piece();
+    } else if (lvalid) {
       const int b = bb + lj;
       const char* qseq = reinterpret_cast<const char*>(q_ptr) + (long long)b * a.s_q * a.h_q * kRowBytes;
       const int m0 = m_lo + kStage * lq;
@@ -401,15 +427,6 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(
         pend = make_rsrc(qseq + (long long)m0 * kRowBytes, rows * kRowBytes);
       }
       ++lq;
-    } else if (lvalid) {
-      const int pidx = lpg + (ltok >> 6) - (lj == 0 ? tb : 0) / kPage;  // position in the page list
-      int page;
-      if (use_list) page = readlane(pidx < 64 ? v_page[0] : v_page[1], pidx & 63);
-      else page = sload_i32(block_table + (long long)(bb + lj) * a.max_blocks + (ltok >> 6));
-      pend = make_rsrc(kv_bytes + ((long long)page * kPage + (ltok & 63)) * row_stride,
-                       kStage * row_stride);
-      ltok += kStage;
-      if (ltok >= lhi) next_piece();
     } else {
       pend = make_rsrc(kv_bytes, 0);
     }
@@ -518,15 +535,16 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(
     // stage in flight are fired at issue points first_slot.. (none if < 0).
     auto pv = [&](const uint32_t* pw, bool rescale, float alpha, int sp, const char MLA_LDS* st,
                   int first_slot) {
-      const int tok0 = lo + sp * kStage;
-      const int nvalid = N - tok0 < kStage ? N - tok0 : kStage;
-      const bool tail = nvalid < kStage;
-      const int nv_lane = nvalid - key_lane;  // valid keys past this lane's first key
+      (void)sp;
+      if (rescale) {
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) acc_scale<OREGS>(o[nt], alpha);
+      }
       if constexpr (R == 32) {
         const i16x8 pb[2] = {__builtin_bit_cast(i16x8, i32x4{(int)pw[0], (int)pw[1], (int)pw[2], (int)pw[3]}),
                              __builtin_bit_cast(i16x8, i32x4{(int)pw[4], (int)pw[5], (int)pw[6], (int)pw[7]})};
         constexpr int NV = 2 * NT;
-        constexpr int VP = 2;
+        constexpr int VP = MLA_VP32;
         // keys 16 kb + 4 h + r (low half) and 16 kb + 8 + 4 h + r (high half)
         auto vread = [&](int idx) {
           const int kb = idx / NT, nb = dg * NT + idx % NT;
@@ -541,21 +559,14 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(
 #pragma unroll
         for (int idx = 0; idx < NV; ++idx) {
           const int kb = idx / NT, nt = idx % NT;
-          i16x8 v = va[idx % VP];
-          if (tail) {
-            const i16x4 v0 = zero_from(i16x4{v[0], v[1], v[2], v[3]}, nv_lane - 16 * kb);
-            const i16x4 v1 = zero_from(i16x4{v[4], v[5], v[6], v[7]}, nv_lane - (16 * kb + 8));
-            v = cat(v0, v1);
-          }
-          if (kb == 0 && rescale) acc_scale<OREGS>(o[nt], alpha);
-          o[nt] = mfma32(v, pb[kb], o[nt]);
+          o[nt] = mfma32(va[idx % VP], pb[kb], o[nt]);
           if (idx + VP < NV) va[idx % VP] = vread(idx + VP);
           if (first_slot >= 0) fire_slot(first_slot + idx);
           __builtin_amdgcn_sched_barrier(0);
         }
       } else {
         const i16x8 pb = __builtin_bit_cast(i16x8, i32x4{(int)pw[0], (int)pw[1], (int)pw[2], (int)pw[3]});
-        constexpr int VP = NT < 4 ? NT : 4;
+        constexpr int VP = NT < MLA_VP16 ? NT : MLA_VP16;
         auto vread = [&](int nt) {
           const int nb = dg * NT + nt;
           const char MLA_LDS* p = st + voff[nb & 3] + 128 * (nb >> 2);
@@ -566,14 +577,7 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(
         for (int j2 = 0; j2 < VP; ++j2) va[j2] = vread(j2);
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
-          i16x8 v = va[nt % VP];
-          if (tail) {
-            const i16x4 v0 = zero_from(i16x4{v[0], v[1], v[2], v[3]}, nv_lane);
-            const i16x4 v1 = zero_from(i16x4{v[4], v[5], v[6], v[7]}, nv_lane - 16);
-            v = cat(v0, v1);
-          }
-          if (rescale) acc_scale<OREGS>(o[nt], alpha);
-          o[nt] = mfma16(v, pb, o[nt]);
+          o[nt] = mfma16(va[nt % VP], pb, o[nt]);
           if (nt + VP < NT) va[nt % VP] = vread(nt + VP);
           if (first_slot >= 0) fire_slot(first_slot + nt);
           __builtin_amdgcn_sched_barrier(0);
@@ -631,7 +635,7 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(
         prep(x, s - 1);
       }
       constexpr int NK = KS_W * KB_W;
-      constexpr int KP = 4;
+      constexpr int KP = NK < (R == 32 ? MLA_KP32 : MLA_KP16) ? NK : (R == 32 ? MLA_KP32 : MLA_KP16);
       auto kaddr = [&](int i) {
         if constexpr (R == 32) return rd + kstep_off(i);
         else {
