@@ -7,10 +7,10 @@
 // were written directly by the main kernel and are skipped here.
 //
 // One wave per query row.  The kernel is latency-bound at small batch, so
-// each wave makes three dependent trips to memory and no more: the split
-// range (scalar loads), the piece LSEs (lane k holds piece k, reduced across
-// the wave), then the partial rows, kUnroll pieces per trip (64 lanes x 8
-// value dims, two 16-byte loads per lane and piece).
+// each wave makes two dependent trips to memory: the split range (scalar
+// loads), then the piece LSEs (lane k holds piece k) together with the partial
+// rows of up to kUnroll pieces (64 lanes x 8 value dims, two 16-byte loads per
+// lane and piece); longer splits take further trips of kUnroll pieces.
 #include "mla_common.hpp"
 #include "mla_internal.hpp"
 
@@ -19,7 +19,7 @@ namespace mla {
 constexpr float kLog2e = 1.44269504088896340736f;
 constexpr float kLn2c = 0.69314718055994530942f;
 constexpr int kCombineRows = 4;  // waves (query rows) per workgroup
-constexpr int kUnroll = 8;       // pieces loaded per trip
+constexpr int kUnroll = 16;      // pieces loaded per trip
 
 __device__ __forceinline__ float wave_max(float x) {
 #pragma unroll
@@ -45,8 +45,19 @@ __global__ __launch_bounds__(64 * kCombineRows) void combine_kernel(CombineArgs 
   const long long r0 = ((long long)s0 * a.h_kv + g) * a.M + m;
   const float* lse_row = a.lse_part + r0;
 
-  // L over all pieces, 64 at a time (lane k holds piece c + k); the first 64
-  // are loaded once and kept.
+  // Issue the first pieces' partial rows with the LSE loads (lane k holds
+  // the LSE of piece c + k), then reduce.
+  const float* o_row = a.o_part + r0 * kValueDim + lane * 8;
+  const int n0 = nsplit < kUnroll ? nsplit : kUnroll;
+  float4 x[kUnroll][2];
+#pragma unroll
+  for (int j = 0; j < kUnroll; ++j) {
+    if (j < n0) {
+      const float4* src = reinterpret_cast<const float4*>(o_row + j * stride * kValueDim);
+      x[j][0] = src[0];
+      x[j][1] = src[1];
+    }
+  }
   auto lse_at = [&](int c) -> float {
     return c + lane < nsplit ? lse_row[(c + lane) * stride] : -INFINITY;
   };
@@ -60,31 +71,29 @@ __global__ __launch_bounds__(64 * kCombineRows) void combine_kernel(CombineArgs 
     float sum = 0.f;
     for (int c = 0; c < nsplit; c += 64) sum += fast_exp2(((c == 0 ? v0 : lse_at(c)) - mx) * kLog2e);
     L = mx + fast_log2(wave_sum(sum)) * kLn2c;
-    const float* o_row = a.o_part + r0 * kValueDim + lane * 8;
-    for (int c = 0; c < nsplit; c += 64) {
+    const float w0 = fast_exp2((v0 - L) * kLog2e);  // weight of piece lane (first 64)
+    auto add = [&](const float4* xj, float wk) {
+      acc[0] += wk * xj[0].x; acc[1] += wk * xj[0].y; acc[2] += wk * xj[0].z; acc[3] += wk * xj[0].w;
+      acc[4] += wk * xj[1].x; acc[5] += wk * xj[1].y; acc[6] += wk * xj[1].z; acc[7] += wk * xj[1].w;
+    };
+#pragma unroll
+    for (int j = 0; j < kUnroll; ++j)
+      if (j < n0) add(x[j], __shfl(w0, j, 64));
+    // pieces past the first kUnroll, kUnroll per trip
+    for (int k0 = kUnroll; k0 < nsplit; k0 += kUnroll) {
+      const int c = k0 & ~63;
       const float wl = fast_exp2(((c == 0 ? v0 : lse_at(c)) - L) * kLog2e);  // weight of piece c + lane
-      const int n = nsplit - c < 64 ? nsplit - c : 64;
-      for (int k0 = 0; k0 < n; k0 += kUnroll) {
-        float4 x[kUnroll][2];
 #pragma unroll
-        for (int j = 0; j < kUnroll; ++j) {
-          if (k0 + j < n) {
-            const float4* src = reinterpret_cast<const float4*>(o_row + (c + k0 + j) * stride * kValueDim);
-            x[j][0] = src[0];
-            x[j][1] = src[1];
-          }
-        }
-#pragma unroll
-        for (int j = 0; j < kUnroll; ++j) {
-          if (k0 + j < n) {
-            const float wk = __shfl(wl, k0 + j, 64);
-            acc[0] += wk * x[j][0].x; acc[1] += wk * x[j][0].y;
-            acc[2] += wk * x[j][0].z; acc[3] += wk * x[j][0].w;
-            acc[4] += wk * x[j][1].x; acc[5] += wk * x[j][1].y;
-            acc[6] += wk * x[j][1].z; acc[7] += wk * x[j][1].w;
-          }
+      for (int j = 0; j < kUnroll; ++j) {
+        if (k0 + j < nsplit) {
+          const float4* src = reinterpret_cast<const float4*>(o_row + (k0 + j) * stride * kValueDim);
+          x[j][0] = src[0];
+          x[j][1] = src[1];
         }
       }
+#pragma unroll
+      for (int j = 0; j < kUnroll; ++j)
+        if (k0 + j < nsplit) add(x[j], __shfl(wl, (k0 + j) & 63, 64));
     }
   }
   const int hpg = a.h_q / a.h_kv;

@@ -179,10 +179,120 @@ __global__ __launch_bounds__(NT) void sched_kernel(const int32_t* __restrict__ s
   }
 }
 
+// Fast variant for up to 1024 sequences and 4096 parts: 256 threads, every
+// per-sequence quantity in LDS, and the first and last sequence of each part
+// found by scattering each sequence's part range (no search, no division per
+// part).  Same output as sched_kernel.
+constexpr int kSmallThreads = 256;
+constexpr int kSmallBatch = 1024;
+constexpr int kSmallParts = 4096;
+
+__global__ __launch_bounds__(kSmallThreads) void sched_small_kernel(
+    const int32_t* __restrict__ seqlens, int batch, int num_parts, int fixed_cost,
+    int32_t* __restrict__ meta, int32_t* __restrict__ num_splits) {
+  __shared__ long long C[kSmallBatch + 1];
+  __shared__ int SL[kSmallBatch], FP[kSmallBatch], LP[kSmallBatch], NS[kSmallBatch];
+  __shared__ int BB[kSmallParts], BE[kSmallParts];
+  __shared__ long long scratch[kSmallThreads / 64];
+  const int tid = threadIdx.x;
+  const int per = (batch + kSmallThreads - 1) / kSmallThreads;
+  const int b0 = tid * per;
+  const long long fc = fixed_cost;
+
+  for (int p = tid; p < num_parts; p += kSmallThreads) {
+    BB[p] = batch;  // no sequence: the part stays empty
+    BE[p] = -1;
+  }
+  long long local = 0;
+  for (int i = 0; i < per; ++i) {
+    const int b = b0 + i;
+    if (b < batch) {
+      const int n = seqlens[b];
+      SL[b] = n;
+      local += units_of(n) + fc;
+    }
+  }
+  long long total;
+  long long base = block_exclusive_scan<kSmallThreads>(local, scratch, &total);
+  long long T = (total + num_parts - 1) / num_parts;
+  if (T < 1) T = 1;
+  // part of cost position x (32-bit division whenever the positions fit)
+  const bool narrow = total < 0x7fffffffLL;
+  auto part_of = [&](long long x) -> int {
+    return narrow ? (int)((unsigned)x / (unsigned)T) : (int)(x / T);
+  };
+  long long pieces = 0;
+  for (int i = 0; i < per; ++i) {
+    const int b = b0 + i;
+    if (b < batch) {
+      C[b] = base;
+      const long long u = units_of(SL[b]);
+      const int first = u > 0 ? part_of(base + fc) : part_of(base + fc - 1);
+      const int last = part_of(base + fc + u - 1);
+      FP[b] = first;
+      LP[b] = last;
+      pieces += last - first + 1;
+      base += u + fc;
+    }
+  }
+  if (tid == 0) C[batch] = total;
+  long long ptotal;
+  long long pbase = block_exclusive_scan<kSmallThreads>(pieces, scratch, &ptotal);
+  for (int i = 0; i < per; ++i) {
+    const int b = b0 + i;
+    if (b < batch) {
+      num_splits[b] = (int32_t)pbase;
+      NS[b] = (int32_t)pbase;
+      pbase += LP[b] - FP[b] + 1;
+    }
+  }
+  if (tid == 0) num_splits[batch] = (int32_t)ptotal;
+  __syncthreads();  // FP, LP, C, NS complete
+
+  // Part p's first sequence is the b with LP[b-1] < p <= LP[b]; its last
+  // sequence is the b with FP[b] <= p < FP[b+1].
+  for (int i = 0; i < per; ++i) {
+    const int b = b0 + i;
+    if (b < batch) {
+      const int plo = b == 0 ? 0 : LP[b - 1] + 1;
+      for (int p = plo; p <= LP[b] && p < num_parts; ++p) BB[p] = b;
+      const int phi = b + 1 < batch ? FP[b + 1] : num_parts;
+      for (int p = FP[b]; p < phi && p < num_parts; ++p) BE[p] = b;
+    }
+  }
+  __syncthreads();
+
+  for (int p = tid; p < num_parts; p += kSmallThreads) {
+    const int bb = BB[p], be = BE[p];
+    i32x4 w0 = {0, 0, -1, 0}, w1 = {0, 0, 0, 0};
+    if (bb < batch && be >= 0 && bb <= be) {
+      const long long lo_key = (long long)p * T, hi_key = (long long)(p + 1) * T;
+      const long long ub = C[bb + 1] - C[bb] - fc;
+      const long long ue = C[be + 1] - C[be] - fc;
+      long long u_begin = 0, u_end = 0;
+      if (ub > 0) {
+        u_begin = lo_key - C[bb] - fc;
+        if (u_begin < 0) u_begin = 0;
+      }
+      if (ue > 0) {
+        u_end = hi_key - C[be] - fc;
+        if (u_end > ue) u_end = ue;
+      }
+      long long tok_end = u_end * kStage;
+      if (tok_end > SL[be]) tok_end = SL[be];
+      w0 = i32x4{bb, (int32_t)(u_begin * kStage), be, (int32_t)tok_end};
+      w1 = i32x4{NS[bb] + (p - FP[bb]), SL[bb], SL[be], NS[be]};
+    }
+    i32x4* dst = reinterpret_cast<i32x4*>(meta + (long long)p * kMetaWords);
+    dst[0] = w0;
+    dst[1] = w1;
+  }
+}
+
 hipError_t launch_sched(const int32_t* seqlens, int batch, int num_parts, int fixed_cost,
                         int32_t* meta, int32_t* num_splits, hipStream_t stream) {
-  if (batch <= 64)
-    hipLaunchKernelGGL((sched_kernel<64, 64>), dim3(1), dim3(64), 0, stream, seqlens, batch,
+  if (batch <= kSmallBatch && num_parts <= kSmallParts)
+    hipLaunchKernelGGL(sched_small_kernel, dim3(1), dim3(kSmallThreads), 0, stream, seqlens, batch,
                        num_parts, fixed_cost, meta, num_splits);
   else if (batch <= 1024)
     hipLaunchKernelGGL((sched_kernel<256, 1024>), dim3(1), dim3(256), 0, stream, seqlens, batch,

@@ -74,12 +74,18 @@ def test_metadata_bitexact():
     import mla_decode_attention_split_amd as mla
     rng = np.random.default_rng(7)
     import torch
-    for trial in range(12):
-        B = int(rng.integers(1, 300))
-        lens = rng.integers(0, 20000, size=B).astype(np.int32)
+    # the last three trials take the scheduler's other two batch/part regimes
+    # (more than 1024 sequences; more than 4096 parts) and the largest batch
+    special = [(2000, 256), (500, 5000), (16384, 256)]
+    for trial in range(12 + len(special)):
+        if trial < 12:
+            B = int(rng.integers(1, 300))
+            num_parts = int(rng.choice([1, 7, 8, 64, 128, 256, 1000]))
+        else:
+            B, num_parts = special[trial - 12]
+        lens = rng.integers(0, 20000 if B < 1000 else 3000, size=B).astype(np.int32)
         if trial % 3 == 0:
             lens[rng.integers(0, B, size=max(1, B // 5))] = 0
-        num_parts = int(rng.choice([1, 7, 8, 64, 128, 256, 1000]))
         fixed_cost = int(rng.integers(1, 8))
         log(f"[case] metadata trial {trial}: B={B} parts={num_parts} fixed={fixed_cost}")
         sl = torch.from_numpy(lens).cuda()
