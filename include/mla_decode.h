@@ -135,7 +135,8 @@ size_t mla_decode_workspace_size(int batch, int q_rows_per_kv_head, int h_kv, in
  *   tile_metadata, num_parts, num_splits  from mla_get_metadata with
  *                  q_rows_per_kv_head = M and the same h_kv
  *   causal         0/1: query t sees keys j <= N - s_q + t
- *   softmax_scale  multiplies the scores (the usual value is 576^-0.5)
+ *   softmax_scale  multiplies the scores; positive and finite (the usual value
+ *                  is 576^-0.5)
  *   out            device bf16 [batch, s_q, h_q, 512], 16-byte aligned,
  *                  rounded to nearest even
  *   lse            device fp32 [batch, s_q, h_q], natural log

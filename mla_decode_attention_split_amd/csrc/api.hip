@@ -167,8 +167,8 @@ int prepare_decode(const void* q, const void* blocked_k, const int32_t* block_ta
                 max_blocks_per_seq);
   if (num_parts < 1 || num_parts > MLA_MAX_PARTS)
     return fail(MLA_ERR_INVALID_ARG, "num_parts %d outside [1, %d]", num_parts, MLA_MAX_PARTS);
-  if (!std::isfinite(softmax_scale))
-    return fail(MLA_ERR_INVALID_ARG, "softmax_scale is not finite");
+  if (!std::isfinite(softmax_scale) || !(softmax_scale > 0.f))
+    return fail(MLA_ERR_INVALID_ARG, "softmax_scale must be positive and finite");
   if (!q || !blocked_k || !block_table || !cache_seqlens || !tile_metadata || !num_splits || !out ||
       !lse || !workspace)
     return fail(MLA_ERR_INVALID_ARG, "null pointer argument");

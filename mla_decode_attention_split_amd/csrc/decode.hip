@@ -231,18 +231,25 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(
     if (j == npieces - 1) return n_last;
     return j < kListPieces ? readlane(v_n, j) : sload_i32(seqlens + bb + j);
   };
-  int v_pages = 0;
-  {
+  // Pages of piece j (lane j) and the position of its first page in the list.
+  int v_pages = 0, v_cum = 0, total_listed, p0 = 0, p1 = 0;
+  if (short_part) {  // scalar: no cross-lane scan before the page loads
+    const int hi0 = bb == be ? te : n_first;
+    p0 = hi0 > tb ? (hi0 + kPage - 1) / kPage - tb / kPage : 0;
+    p1 = (npieces == 2 && te > 0) ? (te + kPage - 1) / kPage : 0;
+    total_listed = p0 + p1;
+  } else {
     const int j = lane;
     if (j < npieces && j < kListPieces) {
       const int lo = j == 0 ? tb : 0;
       const int hi = bb + j == be ? te : (j == 0 ? n_first : v_n);
       v_pages = hi > lo ? (hi + kPage - 1) / kPage - lo / kPage : 0;
     }
+    v_cum = wave_exclusive_sum(v_pages, lane);
+    const int last = (npieces < kListPieces ? npieces : kListPieces) - 1;
+    total_listed = readlane(v_cum, last) + readlane(v_pages, last);
   }
-  const int v_cum = wave_exclusive_sum(v_pages, lane);
   const int listed_pieces = npieces < kListPieces ? npieces : kListPieces;
-  const int total_listed = readlane(v_cum, listed_pieces - 1) + readlane(v_pages, listed_pieces - 1);
   // The page list is used only if it holds every page of the part.
   const bool use_list = npieces <= kListPieces && total_listed <= kListPages;
   int v_page[2] = {0, 0};
@@ -251,9 +258,14 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(
     for (int half = 0; half < 2; ++half) {
       const int i = lane + 64 * half;
       long long idx = -1;
-      for (int j = 0; j < listed_pieces; ++j) {
-        const int c = readlane(v_cum, j), p = readlane(v_pages, j);
-        if (i >= c && i < c + p) idx = (long long)(bb + j) * a.max_blocks + (j == 0 ? tb : 0) / kPage + (i - c);
+      if (short_part) {
+        if (i < p0) idx = (long long)bb * a.max_blocks + tb / kPage + i;
+        else if (i < p0 + p1) idx = (long long)be * a.max_blocks + (i - p0);
+      } else {
+        for (int j = 0; j < listed_pieces; ++j) {
+          const int c = readlane(v_cum, j), p = readlane(v_pages, j);
+          if (i >= c && i < c + p) idx = (long long)(bb + j) * a.max_blocks + (j == 0 ? tb : 0) / kPage + (i - c);
+        }
       }
       if (idx >= 0) v_page[half] = block_table[idx];
     }
@@ -468,14 +480,13 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(
     float m_run = kMinit, l_run = 0.f, lr_run = 0.f;
     i16x8 qf[KS_W];
 
-    // Mask the scores of key stage sp (keys past the end, or past the row's
-    // causal limit) and scale them to the log2 domain.
+    // Mask the raw scores of key stage sp (keys past the end, or past the
+    // row's causal limit).  The scale (positive) is applied later: to the
+    // row max, and inside the exponent's fma.
     auto prep = [&](float* x, int sp) {
       const int tok0 = lo + sp * kStage;
       const int nvalid = N - tok0 < kStage ? N - tok0 : kStage;
       const bool full = tok0 + kStage <= lim_all;  // no key of the stage is masked
-#pragma unroll
-      for (int i = 0; i < SREGS; ++i) x[i] *= a.scale_log2;
       if (!full) {
         const int lim = ((row_lim - tok0 < nvalid) ? row_lim - tok0 : nvalid) - key_lane;
 #pragma unroll
@@ -502,7 +513,7 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(
         st.mx = mx;
       } else if (slice == 1) {
         if constexpr (R == 16) st.mx = max_xor16(st.mx);
-        st.mx = max_xor32(st.mx);
+        st.mx = max_xor32(st.mx) * a.scale_log2;  // = the max of the scaled scores (scale > 0)
       } else if (slice == 2) {
         const bool rs = __any(st.mx > m_run + kTau);
         const float m_new = fmaxf(m_run, st.mx);
@@ -519,7 +530,8 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(
         const bf16x2 ones = __builtin_bit_cast(bf16x2, 0x3f803f80u);
 #pragma unroll
         for (int i = 0; i < 4; i += 2) {
-          const float p0 = fast_exp2(x[e0 + i] - m_run), p1 = fast_exp2(x[e0 + i + 1] - m_run);
+          const float p0 = fast_exp2(__builtin_fmaf(x[e0 + i], a.scale_log2, -m_run));
+          const float p1 = fast_exp2(__builtin_fmaf(x[e0 + i + 1], a.scale_log2, -m_run));
           const uint32_t pk = pack_bf16(p0, p1);
           st.pw[(e0 + i) >> 1] = pk;
           st.sum += p0 + p1;

@@ -86,6 +86,8 @@ def decode_call(**over):
     (dict(out=FAKE + 8), "MLA_ERR_INVALID_ARG"),
     (dict(num_parts=0), "MLA_ERR_INVALID_ARG"),
     (dict(scale=float("nan")), "MLA_ERR_INVALID_ARG"),
+    (dict(scale=0.0), "MLA_ERR_INVALID_ARG"),
+    (dict(scale=-0.0416), "MLA_ERR_INVALID_ARG"),
     (dict(ws_bytes=100), "MLA_ERR_WORKSPACE"),
 ])
 def test_decode_rejects_bad_arguments(over, status):
