@@ -221,7 +221,8 @@ int enqueue_combine(const mla::DecodeArgs& a, hipStream_t st) {
   c.h_q = a.h_q;
   c.h_kv = a.h_kv;
   c.M = a.M;
-  hipError_t e = mla::launch_combine(c, st);
+  c.share_grid = 0;
+  hipError_t e = mla::launch_combine(c, a.num_parts, st);
   if (e != hipSuccess) return fail(MLA_ERR_HIP, "combine launch: %s", hipGetErrorString(e));
   return MLA_OK;
 }
@@ -280,6 +281,7 @@ int mla_decode_combine(const int32_t* num_splits, int batch, int s_q, int h_q, i
   a.h_q = h_q;
   a.h_kv = h_kv;
   a.M = M;
+  a.num_parts = num_parts;
   int rc = enqueue_combine(a, static_cast<hipStream_t>(stream));
   if (rc != MLA_OK) return rc;
   return ok();

@@ -6,11 +6,22 @@
 // empty the row gets out = 0 and lse = -inf.  Sequences with a single piece
 // were written directly by the main kernel and are skipped here.
 //
-// One wave per query row.  The kernel is latency-bound at small batch, so
-// each wave makes two dependent trips to memory: the split range (scalar
-// loads), then the piece LSEs (lane k holds piece k) together with the partial
-// rows of up to kUnroll pieces (64 lanes x 8 value dims, two 16-byte loads per
-// lane and piece); longer splits take further trips of kUnroll pieces.
+// The kernel is latency-bound, so each wave makes two dependent trips to
+// memory: the split range (scalar loads), then the piece LSEs (lane k holds
+// piece k) together with the partial rows of up to kUnroll pieces (64 lanes x
+// 8 value dims, two 16-byte loads per lane and piece).  Two layouts, chosen
+// per sequence from its piece count (so every row of a sequence is summed in
+// the same order):
+//   * one wave per query row, 4 rows per workgroup;
+//   * in the shared-row grid, for sequences of more than kShareMin pieces:
+//     the 4 waves of a workgroup share one row, each taking a 16-aligned
+//     quarter of the pieces, and their sums meet in LDS in wave order.  A row
+//     of 80 pieces then costs two trips per wave instead of five, on 4x as
+//     many CUs.
+// The shared-row grid has one workgroup per query row (in the one-row-per-
+// wave layout only the first ceil(M / 4) of them work); the host picks it
+// when the batch averages many pieces per sequence, since idle workgroups
+// cost dispatch time.
 #include "mla_common.hpp"
 #include "mla_internal.hpp"
 
@@ -18,8 +29,10 @@ namespace mla {
 
 constexpr float kLog2e = 1.44269504088896340736f;
 constexpr float kLn2c = 0.69314718055994530942f;
-constexpr int kCombineRows = 4;  // waves (query rows) per workgroup
-constexpr int kUnroll = 16;      // pieces loaded per trip
+constexpr int kCombineWaves = 4;  // waves per workgroup
+constexpr int kUnroll = 16;       // pieces loaded per trip
+constexpr int kShareMin = 4;      // shared-row grid: more pieces than this, 4 waves per row
+constexpr int kSharePieces = 16;  // pick the shared-row grid at this many pieces per sequence
 
 __device__ __forceinline__ float wave_max(float x) {
 #pragma unroll
@@ -32,28 +45,42 @@ __device__ __forceinline__ float wave_sum(float x) {
   return x;
 }
 
-__global__ __launch_bounds__(64 * kCombineRows) void combine_kernel(CombineArgs a) {
+__global__ __launch_bounds__(64 * kCombineWaves) void combine_kernel(CombineArgs a) {
   const int b = blockIdx.z;
   const int g = blockIdx.y;
   const int s0 = sload_i32(a.num_splits + b);
   const int nsplit = sload_i32(a.num_splits + b + 1) - s0;
-  const int m = blockIdx.x * kCombineRows + (threadIdx.x >> 6);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
-  if (nsplit <= 1 || m >= a.M) return;
+  if (nsplit <= 1) return;
+  const bool shared = a.share_grid && nsplit > kShareMin;  // uniform over the workgroup
+  int m, p_lo, p_hi;                       // this wave's row and pieces [p_lo, p_hi)
+  if (shared) {
+    m = blockIdx.x;
+    if (m >= a.M) return;  // whole workgroup
+    const int q = ((nsplit + kCombineWaves - 1) / kCombineWaves + kUnroll - 1) / kUnroll * kUnroll;
+    p_lo = wave * q < nsplit ? wave * q : nsplit;
+    p_hi = p_lo + q < nsplit ? p_lo + q : nsplit;
+  } else {
+    m = blockIdx.x * kCombineWaves + wave;
+    if (m >= a.M) return;  // this wave only (no barrier in this layout)
+    p_lo = 0;
+    p_hi = nsplit;
+  }
 
   const long long stride = (long long)a.h_kv * a.M;  // rows between consecutive pieces
   const long long r0 = ((long long)s0 * a.h_kv + g) * a.M + m;
   const float* lse_row = a.lse_part + r0;
 
-  // Issue the first pieces' partial rows with the LSE loads (lane k holds
+  // Issue the first trip's partial rows with the LSE loads (lane k holds
   // the LSE of piece c + k), then reduce.
   const float* o_row = a.o_part + r0 * kValueDim + lane * 8;
-  const int n0 = nsplit < kUnroll ? nsplit : kUnroll;
+  const int n0 = p_hi - p_lo < kUnroll ? p_hi - p_lo : kUnroll;
   float4 x[kUnroll][2];
 #pragma unroll
   for (int j = 0; j < kUnroll; ++j) {
     if (j < n0) {
-      const float4* src = reinterpret_cast<const float4*>(o_row + j * stride * kValueDim);
+      const float4* src = reinterpret_cast<const float4*>(o_row + (p_lo + j) * stride * kValueDim);
       x[j][0] = src[0];
       x[j][1] = src[1];
     }
@@ -71,21 +98,27 @@ __global__ __launch_bounds__(64 * kCombineRows) void combine_kernel(CombineArgs 
     float sum = 0.f;
     for (int c = 0; c < nsplit; c += 64) sum += fast_exp2(((c == 0 ? v0 : lse_at(c)) - mx) * kLog2e);
     L = mx + fast_log2(wave_sum(sum)) * kLn2c;
-    const float w0 = fast_exp2((v0 - L) * kLog2e);  // weight of piece lane (first 64)
     auto add = [&](const float4* xj, float wk) {
       acc[0] += wk * xj[0].x; acc[1] += wk * xj[0].y; acc[2] += wk * xj[0].z; acc[3] += wk * xj[0].w;
       acc[4] += wk * xj[1].x; acc[5] += wk * xj[1].y; acc[6] += wk * xj[1].z; acc[7] += wk * xj[1].w;
     };
-#pragma unroll
-    for (int j = 0; j < kUnroll; ++j)
-      if (j < n0) add(x[j], __shfl(w0, j, 64));
-    // pieces past the first kUnroll, kUnroll per trip
-    for (int k0 = kUnroll; k0 < nsplit; k0 += kUnroll) {
+    // Trips start at multiples of kUnroll, so the pieces of one trip share a
+    // 64-piece chunk and one weight register (lane k: piece c + k).
+    auto weights = [&](int k0) {
       const int c = k0 & ~63;
-      const float wl = fast_exp2(((c == 0 ? v0 : lse_at(c)) - L) * kLog2e);  // weight of piece c + lane
+      return fast_exp2(((c == 0 ? v0 : lse_at(c)) - L) * kLog2e);
+    };
+    {
+      const float wl = weights(p_lo);
+#pragma unroll
+      for (int j = 0; j < kUnroll; ++j)
+        if (j < n0) add(x[j], __shfl(wl, (p_lo + j) & 63, 64));
+    }
+    for (int k0 = p_lo + kUnroll; k0 < p_hi; k0 += kUnroll) {
+      const float wl = weights(k0);
 #pragma unroll
       for (int j = 0; j < kUnroll; ++j) {
-        if (k0 + j < nsplit) {
+        if (k0 + j < p_hi) {
           const float4* src = reinterpret_cast<const float4*>(o_row + (k0 + j) * stride * kValueDim);
           x[j][0] = src[0];
           x[j][1] = src[1];
@@ -93,7 +126,24 @@ __global__ __launch_bounds__(64 * kCombineRows) void combine_kernel(CombineArgs 
       }
 #pragma unroll
       for (int j = 0; j < kUnroll; ++j)
-        if (k0 + j < nsplit) add(x[j], __shfl(wl, (k0 + j) & 63, 64));
+        if (k0 + j < p_hi) add(x[j], __shfl(wl, (k0 + j) & 63, 64));
+    }
+  }
+
+  if (shared) {
+    // The four quarter sums meet in LDS and wave 0 adds them in wave order.
+    __shared__ float4 part[kCombineWaves - 1][64][2];
+    if (wave > 0) {
+      part[wave - 1][lane][0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+      part[wave - 1][lane][1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
+    }
+    __syncthreads();
+    if (wave > 0) return;
+#pragma unroll
+    for (int w = 0; w < kCombineWaves - 1; ++w) {
+      const float4 u = part[w][lane][0], v = part[w][lane][1];
+      acc[0] += u.x; acc[1] += u.y; acc[2] += u.z; acc[3] += u.w;
+      acc[4] += v.x; acc[5] += v.y; acc[6] += v.z; acc[7] += v.w;
     }
   }
   const int hpg = a.h_q / a.h_kv;
@@ -109,9 +159,10 @@ __global__ __launch_bounds__(64 * kCombineRows) void combine_kernel(CombineArgs 
   if (lane == 0) a.lse[out_row] = L;
 }
 
-hipError_t launch_combine(const CombineArgs& a, hipStream_t stream) {
-  dim3 grid((a.M + kCombineRows - 1) / kCombineRows, a.h_kv, a.batch);
-  hipLaunchKernelGGL(combine_kernel, grid, dim3(64 * kCombineRows), 0, stream, a);
+hipError_t launch_combine(CombineArgs a, int num_parts, hipStream_t stream) {
+  a.share_grid = (long long)num_parts >= (long long)kSharePieces * a.batch ? 1 : 0;
+  dim3 grid(a.share_grid ? a.M : (a.M + kCombineWaves - 1) / kCombineWaves, a.h_kv, a.batch);
+  hipLaunchKernelGGL(combine_kernel, grid, dim3(64 * kCombineWaves), 0, stream, a);
   return hipGetLastError();
 }
 

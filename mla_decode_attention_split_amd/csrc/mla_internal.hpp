@@ -32,6 +32,7 @@ struct CombineArgs {
   uint16_t* out;
   float* lse;
   int batch, s_q, h_q, h_kv, M;
+  int share_grid;  // 1: one workgroup per query row (set when sequences have many pieces)
 };
 
 // Query rows per workgroup for M rows per KV head (16, 32 or 64; larger M
@@ -41,6 +42,6 @@ inline int tile_rows_for(int M) { return M <= 16 ? 16 : M <= 32 ? 32 : 64; }
 hipError_t launch_sched(const int32_t* seqlens, int batch, int num_parts, int fixed_cost,
                         int32_t* meta, int32_t* num_splits, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, int tile_rows, hipStream_t stream);
-hipError_t launch_combine(const CombineArgs& a, hipStream_t stream);
+hipError_t launch_combine(CombineArgs a, int num_parts, hipStream_t stream);
 
 }  // namespace mla

@@ -106,6 +106,19 @@ def test_split_count_does_not_change_result(num_parts):
     check_parity(out, lse, *ref(w), what=f"parts={num_parts}")
 
 
+@pytest.mark.parametrize("lens,num_parts,h_q,s_q", [([10000], 17, 16, 1), ([10000], 100, 16, 1),
+                                                     ([20000, 50], 129, 32, 2), ([3000, 9000, 1], 160, 16, 3)])
+def test_combine_many_pieces(lens, num_parts, h_q, s_q):
+    """Sequences split into many pieces: the combine's shared-row layout (four
+    waves per row, 16-aligned piece ranges, some of them empty, ranges past
+    the first 64 pieces) against the oracle."""
+    w = synth.make_workload(lens, s_q=s_q, h_q=h_q, causal=s_q > 1, seed=31 + num_parts)
+    case(w, f"many pieces parts={num_parts}")
+    out, lse, _, splits = run_gpu(w, num_parts=num_parts, return_meta=True)
+    assert np.diff(splits).max() > 16  # the shared-row layout is taken
+    check_parity(out, lse, *ref(w), what=f"parts={num_parts}")
+
+
 def test_deterministic_bitwise():
     import torch
     import mla_decode_attention_split_amd as mla
