@@ -34,17 +34,6 @@ constexpr int kUnroll = 16;       // pieces loaded per trip
 constexpr int kShareMin = 4;      // shared-row grid: more pieces than this, 4 waves per row
 constexpr int kSharePieces = 16;  // pick the shared-row grid at this many pieces per sequence
 
-__device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) x = fmaxf(x, __shfl_xor(x, off, 64));
-  return x;
-}
-__device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off, 64);
-  return x;
-}
-
 __global__ __launch_bounds__(64 * kCombineWaves) void combine_kernel(CombineArgs a) {
   const int b = blockIdx.z;
   const int g = blockIdx.y;
@@ -91,19 +80,20 @@ __global__ __launch_bounds__(64 * kCombineWaves) void combine_kernel(CombineArgs
   const float v0 = lse_at(0);
   float mx = v0;
   for (int c = 64; c < nsplit; c += 64) mx = fmaxf(mx, lse_at(c));
-  mx = wave_max(mx);
+  mx = wave_allmax_f32(mx);
   float L = -INFINITY;
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   if (mx > -INFINITY) {
     float sum = 0.f;
     for (int c = 0; c < nsplit; c += 64) sum += fast_exp2(((c == 0 ? v0 : lse_at(c)) - mx) * kLog2e);
-    L = mx + fast_log2(wave_sum(sum)) * kLn2c;
+    L = mx + fast_log2(wave_allsum_f32(sum)) * kLn2c;
     auto add = [&](const float4* xj, float wk) {
       acc[0] += wk * xj[0].x; acc[1] += wk * xj[0].y; acc[2] += wk * xj[0].z; acc[3] += wk * xj[0].w;
       acc[4] += wk * xj[1].x; acc[5] += wk * xj[1].y; acc[6] += wk * xj[1].z; acc[7] += wk * xj[1].w;
     };
     // Trips start at multiples of kUnroll, so the pieces of one trip share a
-    // 64-piece chunk and one weight register (lane k: piece c + k).
+    // 64-piece chunk and one weight register (lane k: piece c + k), read with a
+    // uniform lane index.
     auto weights = [&](int k0) {
       const int c = k0 & ~63;
       return fast_exp2(((c == 0 ? v0 : lse_at(c)) - L) * kLog2e);
@@ -112,7 +102,7 @@ __global__ __launch_bounds__(64 * kCombineWaves) void combine_kernel(CombineArgs
       const float wl = weights(p_lo);
 #pragma unroll
       for (int j = 0; j < kUnroll; ++j)
-        if (j < n0) add(x[j], __shfl(wl, (p_lo + j) & 63, 64));
+        if (j < n0) add(x[j], row_total_f32(wl, (p_lo + j) & 63));
     }
     for (int k0 = p_lo + kUnroll; k0 < p_hi; k0 += kUnroll) {
       const float wl = weights(k0);
@@ -126,7 +116,7 @@ __global__ __launch_bounds__(64 * kCombineWaves) void combine_kernel(CombineArgs
       }
 #pragma unroll
       for (int j = 0; j < kUnroll; ++j)
-        if (k0 + j < p_hi) add(x[j], __shfl(wl, (k0 + j) & 63, 64));
+        if (k0 + j < p_hi) add(x[j], row_total_f32(wl, (k0 + j) & 63));
     }
   }
 

@@ -102,6 +102,15 @@ __device__ __forceinline__ float max_xor32(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
+// x + (x of lane l ^ 32), and of lane l ^ 16 (the same sum in both lanes)
+__device__ __forceinline__ float sum_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float sum_xor16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 __device__ __forceinline__ float max_xor16(float x) {
   const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
@@ -116,17 +125,6 @@ __device__ __forceinline__ void acc_scale(V& o, float s) {
 
 __device__ __forceinline__ i16x8 cat(i16x4 a, i16x4 b) {
   return i16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
-}
-
-// Wave-wide exclusive prefix sum of an int.
-__device__ __forceinline__ int wave_exclusive_sum(int v, int lane) {
-  int x = v;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int y = __shfl_up(x, off, 64);
-    if (lane >= off) x += y;
-  }
-  return x - v;
 }
 
 // Tile shape.  R rows per wave (32x32x16 MFMA for R = 32, 16x16x32 for
@@ -245,7 +243,7 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(
       const int hi = bb + j == be ? te : (j == 0 ? n_first : v_n);
       v_pages = hi > lo ? (hi + kPage - 1) / kPage - lo / kPage : 0;
     }
-    v_cum = wave_exclusive_sum(v_pages, lane);
+    v_cum = wave_inclusive_sum_i32(v_pages) - v_pages;
     const int last = (npieces < kListPieces ? npieces : kListPieces) - 1;
     total_listed = readlane(v_cum, last) + readlane(v_pages, last);
   }
@@ -730,13 +728,11 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(
     // ---- epilogue: normalise and write this piece --------------------------
     float lt = l_run, ltr = lr_run;
     if constexpr (R == 32) {
-      lt += __shfl_xor(lt, 32);
-      ltr += __shfl_xor(ltr, 32);
+      lt = sum_xor32(lt);
+      ltr = sum_xor32(ltr);
     } else {
-      lt += __shfl_xor(lt, 16);
-      lt += __shfl_xor(lt, 32);
-      ltr += __shfl_xor(ltr, 16);
-      ltr += __shfl_xor(ltr, 32);
+      lt = sum_xor32(sum_xor16(lt));
+      ltr = sum_xor32(sum_xor16(ltr));
     }
     const bool empty = !(lt > 0.f);
     const float inv = empty ? 0.f : 1.f / ltr;

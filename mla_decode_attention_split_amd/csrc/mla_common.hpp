@@ -84,6 +84,74 @@ __device__ __forceinline__ int sload_i32(const int32_t* p) {
   return v;
 }
 
+// Cross-lane sums and maxima without the LDS crossbar: DPP row shifts
+// combine the lanes of each row of 16 (Hillis-Steele steps of 1, 2, 4, 8
+// lanes; a lane with fewer than n lanes below it in its row keeps its value),
+// then the row totals held by lanes 15, 31, 47 (and 63) are read into scalar
+// registers and added to the later rows.  All 64 lanes must be active.
+__device__ __forceinline__ int lane_id() {
+  return __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+}
+template <int N>
+__device__ __forceinline__ int row_shr_i32(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, 0x110 + N, 0xf, 0xf, false);
+}
+template <int N>
+__device__ __forceinline__ long long row_shr_i64(long long v) {
+  const unsigned lo = (unsigned)row_shr_i32<N>((int)(unsigned)v);
+  const unsigned hi = (unsigned)row_shr_i32<N>((int)(unsigned)((unsigned long long)v >> 32));
+  return (long long)(((unsigned long long)hi << 32) | lo);
+}
+__device__ __forceinline__ long long readlane_i64(long long v, int l) {
+  const unsigned lo = (unsigned)__builtin_amdgcn_readlane((int)(unsigned)v, l);
+  const unsigned hi = (unsigned)__builtin_amdgcn_readlane((int)(unsigned)((unsigned long long)v >> 32), l);
+  return (long long)(((unsigned long long)hi << 32) | lo);
+}
+// Inclusive prefix sum over the 64 lanes of the wave.
+__device__ __forceinline__ long long wave_inclusive_sum_i64(long long x) {
+  const int r = lane_id() & 15, lane = lane_id();
+#define MLA_ROW_STEP(N) { const long long t = row_shr_i64<N>(x); if (r >= N) x += t; }
+  MLA_ROW_STEP(1) MLA_ROW_STEP(2) MLA_ROW_STEP(4) MLA_ROW_STEP(8)
+#undef MLA_ROW_STEP
+  const long long t0 = readlane_i64(x, 15), t1 = readlane_i64(x, 31), t2 = readlane_i64(x, 47);
+  if (lane >= 16) x += t0;
+  if (lane >= 32) x += t1;
+  if (lane >= 48) x += t2;
+  return x;
+}
+__device__ __forceinline__ int wave_inclusive_sum_i32(int x) {
+  const int r = lane_id() & 15, lane = lane_id();
+#define MLA_ROW_STEP(N) { const int t = row_shr_i32<N>(x); if (r >= N) x += t; }
+  MLA_ROW_STEP(1) MLA_ROW_STEP(2) MLA_ROW_STEP(4) MLA_ROW_STEP(8)
+#undef MLA_ROW_STEP
+  const int t0 = __builtin_amdgcn_readlane(x, 15), t1 = __builtin_amdgcn_readlane(x, 31),
+            t2 = __builtin_amdgcn_readlane(x, 47);
+  if (lane >= 16) x += t0;
+  if (lane >= 32) x += t1;
+  if (lane >= 48) x += t2;
+  return x;
+}
+// The value of x in lane l (l uniform).
+__device__ __forceinline__ float row_total_f32(float x, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), l));
+}
+// Max / sum of x over the 64 lanes of the wave (the same value in every lane).
+__device__ __forceinline__ float wave_allmax_f32(float x) {
+  const int r = lane_id() & 15;
+#define MLA_ROW_STEP(N) { const float t = __int_as_float(row_shr_i32<N>(__float_as_int(x))); if (r >= N) x = fmaxf(x, t); }
+  MLA_ROW_STEP(1) MLA_ROW_STEP(2) MLA_ROW_STEP(4) MLA_ROW_STEP(8)
+#undef MLA_ROW_STEP
+  return fmaxf(fmaxf(row_total_f32(x, 15), row_total_f32(x, 31)),
+               fmaxf(row_total_f32(x, 47), row_total_f32(x, 63)));
+}
+__device__ __forceinline__ float wave_allsum_f32(float x) {
+  const int r = lane_id() & 15;
+#define MLA_ROW_STEP(N) { const float t = __int_as_float(row_shr_i32<N>(__float_as_int(x))); if (r >= N) x += t; }
+  MLA_ROW_STEP(1) MLA_ROW_STEP(2) MLA_ROW_STEP(4) MLA_ROW_STEP(8)
+#undef MLA_ROW_STEP
+  return (row_total_f32(x, 15) + row_total_f32(x, 31)) + (row_total_f32(x, 47) + row_total_f32(x, 63));
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 

@@ -21,25 +21,15 @@ namespace mla {
 
 __device__ __forceinline__ long long units_of(int n) { return ((long long)n + kStage - 1) / kStage; }
 
-// Wave-wide inclusive scan of int64.
-__device__ __forceinline__ long long wave_inclusive_scan(long long x, int lane) {
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const long long y = __shfl_up(x, off, 64);
-    if (lane >= off) x += y;
-  }
-  return x;
-}
-
 // Block-wide exclusive scan of one int64 per thread; *total gets the sum.
 template <int NT>
 __device__ __forceinline__ long long block_exclusive_scan(long long v, long long* scratch,
                                                           long long* total) {
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
-  const long long x = wave_inclusive_scan(v, lane);
+  const long long x = wave_inclusive_sum_i64(v);
   if constexpr (NT == 64) {
-    *total = __shfl(x, 63, 64);
+    *total = readlane_i64(x, 63);
     return x - v;
   } else {
     constexpr int NW = NT / 64;
