@@ -318,6 +318,48 @@ def main():
     torch.cuda.synchronize()
     dec_mean_ms = d0.elapsed_time(d1) / args.steps
 
+    # Pass 3: the metadata call and the combine alone (same buffers), so the
+    # step's parts are reported separately.
+    def span_ms(fn, k):
+        a0 = torch.cuda.Event(enable_timing=True)
+        a1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        torch.cuda._sleep(int(2.4e9 * 0.005))
+        a0.record()
+        for i in range(k):
+            fn(i)
+        a1.record()
+        torch.cuda.synchronize()
+        return a0.elapsed_time(a1) / k
+
+    meta_ms = span_ms(lambda i: mla.mla_get_metadata(sl, M, h_kv, num_parts=num_parts,
+                                                     fixed_cost=fixed_cost, tile_metadata=meta,
+                                                     num_splits=splits), 200)
+    comb_ms = span_ms(lambda i: mla.mla_decode_combine(splits, out, lse, ws, num_parts=num_parts,
+                                                       h_kv=h_kv), 200)
+
+    # Pass 4: ceilings measured on this GPU.  (a) The pages this workload
+    # reads, streamed through the main kernel's LDS ring with no arithmetic,
+    # over the same rotating pool copies; (b) a loop of independent bf16
+    # MFMAs on every SIMD.
+    used = [p for b in range(w.batch) for p in w.block_table[b, :(int(w.seqlens[b]) + 63) // 64]]
+    groups = 256
+    per = max(1, (len(used) + groups - 1) // groups)
+    plist = np.full(groups * per, w.kcache.shape[0], dtype=np.int32)  # padding: outside the pool
+    plist[:len(used)] = np.asarray(used, dtype=np.int32)
+    pages_t = torch.from_numpy(plist.reshape(groups, per)).to(dev)
+    isink = torch.zeros(1, dtype=torch.int32, device=dev)
+    fsink = torch.zeros(1, dtype=torch.float32, device=dev)
+    kv_pages = [kc.view(kc.shape[0], -1) for kc in kvs]
+    for i in range(3):
+        mla.mla_ceiling_stream(kv_pages[i % copies], pages_t, isink)
+    stream_ms = span_ms(lambda i: mla.mla_ceiling_stream(kv_pages[i % copies], pages_t, isink), 100)
+    stream_tbs = len(used) * 64 * 1152 / (stream_ms * 1e-3) / 1e12
+    mf_wg, mf_it = 1024, 1000
+    mla.mla_ceiling_mfma(fsink, mf_wg, mf_it)
+    mfma_ms = span_ms(lambda i: mla.mla_ceiling_mfma(fsink, mf_wg, mf_it), 20)
+    mfma_tflops = mf_wg * 4 * mf_it * 4 * 32768 / (mfma_ms * 1e-3) / 1e12
+
     value_tbs = nbytes / (ms_per_step * 1e-3) / 1e12
     hbm_bound = args.workload != "mtp"
     if hbm_bound:
@@ -338,6 +380,12 @@ def main():
     eprint(f"decode kernel {dec_mean_ms * 1e3:.2f} us mean over {args.steps} back-to-back launches "
            f"-> {achieved:.1f} {roof['unit']} "
            f"({roof['frac'] * 100:.1f}% of peak)")
+    ceil_val = stream_tbs * 1e3 if hbm_bound else mfma_tflops
+    eprint(f"metadata call {meta_ms * 1e3:.2f} us, combine {comb_ms * 1e3:.2f} us (each alone)")
+    eprint(f"measured ceilings: paged stream {stream_tbs:.3f} TB/s ({len(used)} pages, "
+           f"{stream_ms * 1e3:.2f} us), bf16 MFMA loop {mfma_tflops:.1f} TFLOP/s; decode kernel at "
+           f"{achieved / ceil_val * 100:.1f}% of the measured "
+           f"{'stream' if hbm_bound else 'MFMA'} ceiling")
 
     result = {
         "metric": METRIC,
@@ -359,6 +407,16 @@ def main():
         "tflops": round(flops / (ms_per_step * 1e-3) / 1e12, 3),
         "decode_kernel_us": round(dec_mean_ms * 1e3, 3),
         "roofline": roof,
+        "parts_us": {"metadata": round(meta_ms * 1e3, 3), "decode": round(dec_mean_ms * 1e3, 3),
+                     "combine": round(comb_ms * 1e3, 3)},
+        "measured_ceilings": {
+            "stream_read": {"value": round(stream_tbs, 4), "unit": "TB/s",
+                            "what": "the workload's cache pages through the main kernel's LDS "
+                                    "ring, no arithmetic, rotating pool copies"},
+            "mfma_bf16": {"value": round(mfma_tflops, 1), "unit": "TFLOP/s",
+                          "what": "independent 32x32x16 bf16 MFMA chains on every SIMD"},
+            "decode_frac": round(achieved / ceil_val, 4),
+        },
     }
     if not args.no_cpu_baseline:
         eprint("cpu baseline (oracle) ...")

@@ -178,6 +178,36 @@ int mla_decode_combine(const int32_t *num_splits, int batch, int s_q, int h_q, i
                        int num_parts, void *out, float *lse, const void *workspace,
                        size_t workspace_bytes, void *stream);
 
+/* ---- Measurement helpers (not part of the decode path) --------------------
+ * Ceilings measured on the running machine, against which the main kernel's
+ * throughput is quoted besides the datasheet peaks.  They compute nothing of
+ * the method; the benchmark is their only caller.
+ *
+ * mla_ceiling_stream: each of num_workgroups workgroups streams the
+ * pages_per_workgroup cache pages listed in
+ * pages[w * pages_per_workgroup + i] through a 4-slot LDS ring of
+ * 36,864-byte stages with 16-byte LDS-DMA loads, two stages ahead, as the main
+ * kernel's 16-row tile does; no arithmetic.
+ *   pool        device, num_pages pages of page_bytes bytes (one KV head)
+ *   page_bytes  must be 73,728 (64 rows x 1152 B); num_pages * page_bytes
+ *               must be below 2^31; a page index outside the pool loads
+ *               zeros (no fault)
+ *   pages       device int32 [num_workgroups, pages_per_workgroup]
+ *   sink        device int32 [1]; written only in a case that does not occur
+ *               for real data (it keeps the loads from being optimised away)
+ * Bytes read = num_workgroups * pages_per_workgroup * page_bytes.
+ *
+ * mla_ceiling_mfma: num_workgroups workgroups of 4 waves; each wave runs
+ * iters x 4 independent 32x32x16 bf16 MFMAs (32768 flops each).
+ *   sink   device float [1], same role as above
+ * Flops = num_workgroups * 4 * iters * 4 * 32768.
+ * Both return MLA_ERR_INVALID_ARG for null pointers or sizes outside the
+ * stated ranges and enqueue on `stream`.
+ */
+int mla_ceiling_stream(const void *pool, int num_pages, int page_bytes, const int32_t *pages,
+                       int num_workgroups, int pages_per_workgroup, int32_t *sink, void *stream);
+int mla_ceiling_mfma(float *sink, int num_workgroups, int iters, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -75,6 +75,10 @@ def _load():
     lib.mla_decode_splitkv.restype = i
     lib.mla_decode_combine.argtypes = [p, i, i, i, i, i, p, p, p, sz, p]
     lib.mla_decode_combine.restype = i
+    lib.mla_ceiling_stream.argtypes = [p, i, i, p, i, i, p, p]
+    lib.mla_ceiling_stream.restype = i
+    lib.mla_ceiling_mfma.argtypes = [p, i, i, p]
+    lib.mla_ceiling_mfma.restype = i
     _lib = lib
     return lib
 
@@ -220,6 +224,27 @@ def mla_decode_combine(num_splits, out, lse, workspace, *, num_parts: int, h_kv:
             lse.data_ptr(), workspace.data_ptr(), workspace.numel() * workspace.element_size(),
             _stream_of(out.device)))
     return out, lse
+
+
+def mla_ceiling_stream(pool, pages, sink):
+    """Measurement helper: stream the cache pages listed in ``pages`` (int32
+    ``[workgroups, pages_per_workgroup]``) of ``pool`` (bf16
+    ``[num_pages, 64, 1, 576]``) through the main kernel's LDS ring, no
+    arithmetic.  ``sink`` is an int32 device tensor of one element."""
+    W, P = pages.shape
+    with _torch_device(pool.device):
+        _check(_load().mla_ceiling_stream(
+            pool.data_ptr(), int(pool.shape[0]), pool[0].numel() * pool.element_size(),
+            pages.data_ptr(), int(W), int(P), sink.data_ptr(), _stream_of(pool.device)))
+
+
+def mla_ceiling_mfma(sink, num_workgroups: int, iters: int):
+    """Measurement helper: ``num_workgroups`` x 4 waves of ``iters`` x 4
+    independent 32x32x16 bf16 MFMAs.  ``sink`` is a float device tensor of
+    one element."""
+    with _torch_device(sink.device):
+        _check(_load().mla_ceiling_mfma(sink.data_ptr(), int(num_workgroups), int(iters),
+                                        _stream_of(sink.device)))
 
 
 def _torch_device(dev):

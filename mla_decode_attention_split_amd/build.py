@@ -14,7 +14,7 @@ from concurrent.futures import ThreadPoolExecutor
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmla_decode.so")
-SOURCES = ["api.hip", "sched.hip", "decode.hip", "combine.hip"]
+SOURCES = ["api.hip", "sched.hip", "decode.hip", "combine.hip", "ceiling.hip"]
 ARCH = os.environ.get("MLA_OFFLOAD_ARCH", "gfx950")
 
 COMMON = [

@@ -308,4 +308,31 @@ int mla_decode(const void* q, const void* blocked_k, const int32_t* block_table,
   return ok();
 }
 
+int mla_ceiling_stream(const void* pool, int num_pages, int page_bytes, const int32_t* pages,
+                       int num_workgroups, int pages_per_workgroup, int32_t* sink, void* stream) {
+  if (!pool || !pages || !sink) return fail(MLA_ERR_INVALID_ARG, "null pointer argument");
+  if (page_bytes != 2 * mla::kStageBytes)
+    return fail(MLA_ERR_INVALID_ARG, "page_bytes %d != %d", page_bytes, 2 * mla::kStageBytes);
+  if (num_pages < 1 || (long long)num_pages * page_bytes >= (1LL << 31))
+    return fail(MLA_ERR_INVALID_ARG, "num_pages %d outside [1, 2^31 / page_bytes)", num_pages);
+  if (num_workgroups < 1 || num_workgroups > (1 << 20) || pages_per_workgroup < 1 ||
+      pages_per_workgroup > (1 << 16))
+    return fail(MLA_ERR_INVALID_ARG, "num_workgroups %d, pages_per_workgroup %d", num_workgroups,
+                pages_per_workgroup);
+  hipError_t e = mla::launch_stream_ceiling(pool, (unsigned)((long long)num_pages * page_bytes), pages,
+                                            num_workgroups, pages_per_workgroup, sink,
+                                            static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(MLA_ERR_HIP, "stream ceiling launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+int mla_ceiling_mfma(float* sink, int num_workgroups, int iters, void* stream) {
+  if (!sink) return fail(MLA_ERR_INVALID_ARG, "null pointer argument");
+  if (num_workgroups < 1 || num_workgroups > (1 << 20) || iters < 1 || iters > (1 << 24))
+    return fail(MLA_ERR_INVALID_ARG, "num_workgroups %d, iters %d", num_workgroups, iters);
+  hipError_t e = mla::launch_mfma_ceiling(sink, num_workgroups, iters, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(MLA_ERR_HIP, "mfma ceiling launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
 }  // extern "C"

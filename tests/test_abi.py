@@ -111,3 +111,19 @@ def test_metadata_rejects_bad_arguments():
 def test_binding_rejects_wrong_value_dim():
     with pytest.raises(mla.MlaError):
         mla.flash_mla_with_kvcache(None, None, None, None, 256, None, None)
+
+
+def test_ceiling_helpers_reject_bad_arguments():
+    """The measurement helpers check their arguments on the host (no GPU call)."""
+    lib = mla._load()
+    c = header_constants()
+    bad = c["MLA_ERR_INVALID_ARG"]
+    page = 64 * 1152
+    assert lib.mla_ceiling_stream(None, 8, page, FAKE, 4, 2, FAKE, None) == bad
+    assert lib.mla_ceiling_stream(FAKE, 8, page // 2, FAKE, 4, 2, FAKE, None) == bad
+    assert lib.mla_ceiling_stream(FAKE, (1 << 31) // page + 1, page, FAKE, 4, 2, FAKE, None) == bad
+    assert lib.mla_ceiling_stream(FAKE, 8, page, FAKE, 0, 2, FAKE, None) == bad
+    assert lib.mla_ceiling_stream(FAKE, 8, page, FAKE, 4, 0, FAKE, None) == bad
+    assert lib.mla_ceiling_mfma(None, 4, 10, None) == bad
+    assert lib.mla_ceiling_mfma(FAKE, 0, 10, None) == bad
+    assert lib.mla_ceiling_mfma(FAKE, 4, 0, None) == bad

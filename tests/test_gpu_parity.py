@@ -193,3 +193,20 @@ def test_full_size_sampled(name, seqs):
     check_parity(out[seqs], lse[seqs], rout, rlse, what=f"{name} seqs {seqs}")
     assert np.isfinite(out).all()
     assert np.isfinite(lse).all()
+
+
+def test_ceiling_helpers_run():
+    """The measurement helpers run on a small pool, including page indices
+    outside it (which must load nothing rather than fault)."""
+    import torch
+    import mla_decode_attention_split_amd as mla
+    log("case: ceiling helpers")
+    dev = torch.device("cuda")
+    pool = torch.zeros((16, 64 * 576), dtype=torch.bfloat16, device=dev)
+    pages = torch.tensor([[0, 5, 15], [3, 16, 1 << 30]], dtype=torch.int32, device=dev)
+    isink = torch.zeros(1, dtype=torch.int32, device=dev)
+    fsink = torch.zeros(1, dtype=torch.float32, device=dev)
+    mla.mla_ceiling_stream(pool, pages, isink)
+    mla.mla_ceiling_mfma(fsink, 8, 10)
+    torch.cuda.synchronize()
+    assert int(isink.item()) == 0 and float(fsink.item()) == 0.0
