@@ -49,6 +49,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
+SIMDS = 256 * 4  # MI355X: 256 CUs of 4 SIMDs
+XCDS = 8
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
 COUNTERS = os.path.join(ROOT, "profiles", "decode_kernel_counters.json")
@@ -191,8 +193,49 @@ def summarize_profiles(d):
                           f"WRITE_SIZE x{cal['WRITE_SIZE']['scale']:.4f} (1 GiB torch copy read/written 5 times)",
                       f"decode kernel HBM bytes per launch: read {entry['hbm_read_bytes_per_launch'] / 1e6:.2f} MB, "
                       f"write {entry['hbm_write_bytes_per_launch'] / 1e6:.2f} MB"]
+        sq_path = os.path.join(d, f"pmc_SQ_{wl}", "run_counter_collection.csv")
+        if os.path.exists(sq_path):
+            per = {}
+            for r in _csv_rows(sq_path):
+                if "decode_kernel" in r["Kernel_Name"]:
+                    per.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+            mean = {k: sum(v) / len(v) for k, v in per.items()}
+            lines += ["", "SQ counters of the decode kernel (separate run, --steps 5 --warmup 2; mean per "
+                          "dispatch):",
+                      f"  command: rocprofv3 --pmc SQ_WAVES SQ_WAVE_CYCLES SQ_BUSY_CYCLES "
+                      f"SQ_VALU_MFMA_BUSY_CYCLES SQ_LDS_BANK_CONFLICT SQ_INSTS_LDS SQ_WAIT_INST_ANY "
+                      f"SQ_ACTIVE_INST_ANY GRBM_GUI_ACTIVE -d DIR/pmc_SQ_{wl} -o run --output-format csv -- "
+                      f"python3 /root/repo/bench.py --workload {wl} --steps 5 --warmup 2 --no-cpu-baseline"]
+            for k in sorted(mean):
+                lines.append(f"  {k:28s} {mean[k]:16.1f}")
+            if mean.get("GRBM_GUI_ACTIVE") and "SQ_VALU_MFMA_BUSY_CYCLES" in mean:
+                # GRBM_GUI_ACTIVE is summed over the XCDs; SQ_VALU_MFMA_BUSY_CYCLES over all
+                # SIMDs (it reads 32 cycles per 32x32x16 MFMA).
+                active = mean["GRBM_GUI_ACTIVE"] / XCDS
+                util = mean["SQ_VALU_MFMA_BUSY_CYCLES"] / (active * SIMDS)
+                lines.append(f"  MFMA busy fraction = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / {XCDS} "
+                             f"XCDs x {SIMDS} SIMDs) = {util:.3f}")
+                dec = [r for r in stats if "decode_kernel" in r["Name"]]
+                if dec:
+                    ns = float(dec[0]["AverageNs"])
+                    lines.append(f"  GRBM_GUI_ACTIVE / {XCDS} / mean kernel time ({ns / 1e3:.2f} us, kernel "
+                                 f"trace) = {active / ns:.2f} GHz (the counter window also spans the "
+                                 f"dispatch, so for short kernels this overstates the shader clock and "
+                                 f"understates the MFMA busy fraction)")
+                if entry:
+                    entry["mfma_busy_frac"] = round(util, 4)
+            if mean.get("SQ_INSTS_LDS"):
+                lines.append(f"  LDS bank-conflict cycles per LDS instruction = "
+                             f"{mean.get('SQ_LDS_BANK_CONFLICT', 0.0) / mean['SQ_INSTS_LDS']:.4f}")
         with open(os.path.join(out_dir, f"decode_kernel_{wl}.txt"), "w") as f:
             f.write("\n".join(lines) + "\n")
+    clocks = os.path.join(d, "clocks.txt")
+    if os.path.exists(clocks):
+        keep = [x for x in open(clocks).read().splitlines() if "clk" in x.lower() or "GPU[" in x]
+        with open(os.path.join(out_dir, "gpu_clocks.txt"), "w") as f:
+            f.write("# rocm-smi --showclocks on the GPU box, idle, before the profiled runs (the clock under\n"
+                    "# load is derived from counters in decode_kernel_<workload>.txt)\n")
+            f.write("\n".join(keep) + "\n")
     with open(COUNTERS, "w") as f:
         json.dump(counters, f, indent=1)
         f.write("\n")
