@@ -117,6 +117,47 @@ def cpu_baseline(w, min_seconds=10.0):
                       f"runs of {med:.3f} s, fp64"}
 
 
+def torch_baseline(w, q, kv, bt, out_ref, steps=10):
+    """Plain PyTorch on the GPU, for context: gather every sequence's pages
+    into a padded dense K (B, Nmax, 576), scores as one batched bf16 product,
+    masked softmax in fp32, P (bf16) times V.  One KV head only.  Every
+    operand of a bf16 batched product is made contiguous first."""
+    import torch
+    B, s_q, h_q = w.batch, w.s_q, w.h_q
+    M = s_q * h_q
+    n = torch.from_numpy(w.seqlens.astype(np.int64)).to(q.device)
+    pmax = int((int(w.seqlens.max()) + 63) // 64)
+    jj = torch.arange(pmax * 64, device=q.device)
+    row_t = torch.arange(M, device=q.device) // h_q
+    lim = n[:, None] - s_q + row_t[None, :] + 1 if w.causal else n[:, None].expand(B, M)
+    lim = torch.minimum(lim, n[:, None])
+    masked = jj[None, :, None] >= lim[:, None, :]                       # (B, Nmax, M)
+    pages = kv.view(kv.shape[0], 64, 576)
+
+    def run():
+        K = pages[bt[:, :pmax].long()].reshape(B, pmax * 64, 576)        # gather
+        qT = q.reshape(B, M, 576).transpose(1, 2).contiguous()             # (B, 576, M)
+        St = torch.bmm(K, qT).float() * w.scale                            # (B, Nmax, M)
+        St = St.masked_fill(masked, float("-inf"))
+        lse = torch.logsumexp(St, dim=1)                                   # (B, M)
+        P = torch.exp(St - lse[:, None, :]).transpose(1, 2).contiguous().to(torch.bfloat16)
+        V = K[:, :, :512].contiguous()
+        return torch.bmm(P, V), lse                                        # (B, M, 512)
+
+    o, _ = run()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        run()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    diff = (o.float().reshape(B, s_q, h_q, 512) - out_ref.float()).abs().max().item()
+    return ms, diff
+
+
 def _csv_rows(path):
     import csv
     with open(path) as f:
@@ -248,10 +289,12 @@ def main():
     ap.add_argument("--steps", type=int, default=500)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default="membound",
-                    choices=["tiny", "membound", "mtp", "large", "ragged"])
+                    choices=["tiny", "membound", "mtp", "large", "ragged", "hkv2"])
     ap.add_argument("--rotate-bytes", type=float, default=float(1 << 30),
                     help="total bytes of KV pool copies the steps rotate over")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--torch-baseline", action="store_true",
+                    help="also time a plain PyTorch implementation on the GPU (context)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (to scale HBM counters)")
     ap.add_argument("--summarize-profiles", metavar="DIR",
@@ -393,11 +436,13 @@ def main():
     pages_t = torch.from_numpy(plist.reshape(groups, per)).to(dev)
     isink = torch.zeros(1, dtype=torch.int32, device=dev)
     fsink = torch.zeros(1, dtype=torch.float32, device=dev)
-    kv_pages = [kc.view(kc.shape[0], -1) for kc in kvs]
-    for i in range(3):
-        mla.mla_ceiling_stream(kv_pages[i % copies], pages_t, isink)
-    stream_ms = span_ms(lambda i: mla.mla_ceiling_stream(kv_pages[i % copies], pages_t, isink), 100)
-    stream_tbs = len(used) * 64 * 1152 / (stream_ms * 1e-3) / 1e12
+    stream_tbs = None
+    if h_kv == 1:  # the ring streams pages of one KV head
+        kv_pages = [kc.view(kc.shape[0], -1) for kc in kvs]
+        for i in range(3):
+            mla.mla_ceiling_stream(kv_pages[i % copies], pages_t, isink)
+        stream_ms = span_ms(lambda i: mla.mla_ceiling_stream(kv_pages[i % copies], pages_t, isink), 100)
+        stream_tbs = len(used) * 64 * 1152 / (stream_ms * 1e-3) / 1e12
     mf_wg, mf_it = 1024, 1000
     mla.mla_ceiling_mfma(fsink, mf_wg, mf_it)
     mfma_ms = span_ms(lambda i: mla.mla_ceiling_mfma(fsink, mf_wg, mf_it), 20)
@@ -423,12 +468,16 @@ def main():
     eprint(f"decode kernel {dec_mean_ms * 1e3:.2f} us mean over {args.steps} back-to-back launches "
            f"-> {achieved:.1f} {roof['unit']} "
            f"({roof['frac'] * 100:.1f}% of peak)")
-    ceil_val = stream_tbs * 1e3 if hbm_bound else mfma_tflops
+    ceil_val = (stream_tbs * 1e3 if stream_tbs else None) if hbm_bound else mfma_tflops
     eprint(f"metadata call {meta_ms * 1e3:.2f} us, combine {comb_ms * 1e3:.2f} us (each alone)")
-    eprint(f"measured ceilings: paged stream {stream_tbs:.3f} TB/s ({len(used)} pages, "
-           f"{stream_ms * 1e3:.2f} us), bf16 MFMA loop {mfma_tflops:.1f} TFLOP/s; decode kernel at "
-           f"{achieved / ceil_val * 100:.1f}% of the measured "
-           f"{'stream' if hbm_bound else 'MFMA'} ceiling")
+    if stream_tbs:
+        eprint(f"measured ceilings: paged stream {stream_tbs:.3f} TB/s ({len(used)} pages, "
+               f"{stream_ms * 1e3:.2f} us), bf16 MFMA loop {mfma_tflops:.1f} TFLOP/s")
+    else:
+        eprint(f"measured ceilings: bf16 MFMA loop {mfma_tflops:.1f} TFLOP/s (stream ceiling: one KV head only)")
+    if ceil_val:
+        eprint(f"decode kernel at {achieved / ceil_val * 100:.1f}% of the measured "
+               f"{'stream' if hbm_bound else 'MFMA'} ceiling")
 
     result = {
         "metric": METRIC,
@@ -453,14 +502,26 @@ def main():
         "parts_us": {"metadata": round(meta_ms * 1e3, 3), "decode": round(dec_mean_ms * 1e3, 3),
                      "combine": round(comb_ms * 1e3, 3)},
         "measured_ceilings": {
-            "stream_read": {"value": round(stream_tbs, 4), "unit": "TB/s",
+            "stream_read": None if stream_tbs is None else {"value": round(stream_tbs, 4), "unit": "TB/s",
                             "what": "the workload's cache pages through the main kernel's LDS "
                                     "ring, no arithmetic, rotating pool copies"},
             "mfma_bf16": {"value": round(mfma_tflops, 1), "unit": "TFLOP/s",
                           "what": "independent 32x32x16 bf16 MFMA chains on every SIMD"},
-            "decode_frac": round(achieved / ceil_val, 4),
+            "decode_frac": round(achieved / ceil_val, 4) if ceil_val else None,
         },
     }
+    if args.torch_baseline and h_kv == 1:
+        step(0)
+        torch.cuda.synchronize()
+        t_ms, t_diff = torch_baseline(w, q, kvs[0], bt, out)
+        result["gpu_torch_baseline"] = {
+            "value": round(nbytes / (t_ms * 1e-3) / 1e12, 4), "unit": "TB/s",
+            "tflops": round(flops / (t_ms * 1e-3) / 1e12, 2), "ms": round(t_ms, 4),
+            "max_abs_diff_vs_kernel": t_diff,
+            "what": "PyTorch on the GPU: padded dense gather of the pages, bf16 batched products, "
+                    "fp32 masked softmax; pool already warm in cache"}
+        eprint(f"torch baseline {t_ms * 1e3:.1f} us per call ({nbytes / (t_ms * 1e-3) / 1e12:.3f} TB/s), "
+               f"max |diff| vs kernel {t_diff:.3g}")
     if not args.no_cpu_baseline:
         eprint("cpu baseline (oracle) ...")
         result["cpu_baseline"] = cpu_baseline(w)

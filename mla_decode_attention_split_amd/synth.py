@@ -32,7 +32,7 @@ DV = 512
 PAGE = 64
 BF16_NAN = np.uint16(0x7FC0)
 
-WORKLOADS = ("tiny", "membound", "mtp", "large", "ragged")
+WORKLOADS = ("tiny", "membound", "mtp", "large", "ragged", "hkv2")
 
 
 def bf16_bits(x: np.ndarray) -> np.ndarray:
@@ -127,7 +127,7 @@ def make_workload(seqlens, *, s_q: int = 1, h_q: int = 16, h_kv: int = 1, causal
 
 
 def named_workload(name: str, seed: int | None = None) -> Workload:
-    """One of the five named workloads (seed defaults to its index)."""
+    """One of the named workloads (seed defaults to its index)."""
     idx = WORKLOADS.index(name)
     seed = idx if seed is None else seed
     if name == "tiny":
@@ -152,5 +152,7 @@ def named_workload(name: str, seed: int | None = None) -> Workload:
         lens[0] = 32768
         lens[8] = 32768
         return make_workload(lens.astype(np.int32), s_q=1, h_q=64, seed=seed, name=name)
+    if name == "hkv2":  # two latent KV heads, 16 query heads each
+        return make_workload(np.full(32, 4096), s_q=1, h_q=32, h_kv=2, seed=seed, name=name)
     raise KeyError(name)
 

@@ -53,7 +53,7 @@ def test_random_small_shapes(seed):
 
 
 @pytest.mark.parametrize("h_q,s_q", [(8, 1), (24, 1), (40, 1), (16, 3), (48, 3), (128, 3),
-                                     (96, 1), (16, 8)])
+                                     (96, 1), (16, 8), (64, 8), (128, 8)])
 def test_row_tile_boundaries(h_q, s_q):
     w = synth.make_workload([130, 77, 300], s_q=s_q, h_q=h_q, causal=True, seed=h_q + s_q)
     case(w, f"rows {s_q * h_q}")
@@ -181,7 +181,8 @@ def test_constant_value_rows():
 
 
 @pytest.mark.parametrize("name,seqs", [("membound", [0, 13, 31]), ("mtp", [0, 17, 63]),
-                                       ("large", [0, 64, 127]), ("ragged", [0, 3, 8, 11])])
+                                       ("large", [0, 64, 127]), ("ragged", [0, 3, 8, 11]),
+                                       ("hkv2", [0, 19, 31])])
 def test_full_size_sampled(name, seqs):
     """Full-size workload in the benchmark's launch configuration; the oracle
     recomputes whole sequences of it (the same pages and queries)."""
