@@ -108,7 +108,8 @@ def cpu_baseline(w, min_seconds=10.0):
     t_end = time.perf_counter() + min_seconds
     while time.perf_counter() < t_end or len(times) < 3:
         t0 = time.perf_counter()
-        oracle.decode(w.q, w.kcache, w.block_table, w.seqlens, causal=w.causal, scale=w.scale)
+        oracle.decode(w.q, w.kcache, w.block_table, w.seqlens, causal=w.causal, scale=w.scale,
+                      dtype=w.dtype)
         times.append(time.perf_counter() - t0)
     med = statistics.median(times)
     return {"value": nbytes / med / 1e12, "unit": "TB/s", "cores": oracle.num_threads(),
@@ -290,6 +291,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default="membound",
                     choices=["tiny", "membound", "mtp", "large", "ragged", "hkv2"])
+    ap.add_argument("--dtype", default="bf16", choices=["bf16", "fp16"],
+                    help="element type of q, the cache and out")
     ap.add_argument("--rotate-bytes", type=float, default=float(1 << 30),
                     help="total bytes of KV pool copies the steps rotate over")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -330,7 +333,7 @@ def main():
     import mla_decode_attention_split_amd as mla
     from mla_decode_attention_split_amd import synth
 
-    w = synth.named_workload(args.workload)
+    w = synth.named_workload(args.workload, dtype=args.dtype)
     nbytes, flops = algorithmic_units(w)
     M, h_kv = w.rows_per_kv_head, w.h_kv
     pool_bytes = w.kcache.nbytes
@@ -339,15 +342,16 @@ def main():
            f"causal={w.causal} sum(N)={int(w.seqlens.sum())} bytes={nbytes / 1e6:.2f} MB "
            f"flops={flops / 1e9:.2f} GFLOP pool={pool_bytes / 1e6:.1f} MB x{copies} copies")
 
-    q = torch.from_numpy(w.q.view(np.int16)).to(dev).view(torch.bfloat16)
-    kv0 = torch.from_numpy(w.kcache.view(np.int16)).to(dev).view(torch.bfloat16)
+    tdt = torch.float16 if args.dtype == "fp16" else torch.bfloat16
+    q = torch.from_numpy(w.q.view(np.int16)).to(dev).view(tdt)
+    kv0 = torch.from_numpy(w.kcache.view(np.int16)).to(dev).view(tdt)
     kvs = [kv0] + [kv0.clone() for _ in range(copies - 1)]
     bt = torch.from_numpy(np.ascontiguousarray(w.block_table)).to(dev)
     sl = torch.from_numpy(np.ascontiguousarray(w.seqlens)).to(dev)
     num_parts, fixed_cost, tile_rows = mla.mla_get_metadata_shape(w.batch, M, h_kv)
     meta = torch.empty((num_parts, 8), dtype=torch.int32, device=dev)
     splits = torch.empty((w.batch + 1,), dtype=torch.int32, device=dev)
-    out = torch.empty((w.batch, w.s_q, w.h_q, 512), dtype=torch.bfloat16, device=dev)
+    out = torch.empty((w.batch, w.s_q, w.h_q, 512), dtype=tdt, device=dev)
     lse = torch.empty((w.batch, w.s_q, w.h_q), dtype=torch.float32, device=dev)
     ws = torch.empty((mla.mla_decode_workspace_size(w.batch, M, h_kv, num_parts),),
                      dtype=torch.uint8, device=dev)
@@ -490,7 +494,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": args.dtype,
         "data": "synthetic",
         "config": {"workload": w.name, "batch": w.batch, "s_q": w.s_q, "h_q": w.h_q,
                    "h_kv": h_kv, "seqlens_sum": int(w.seqlens.sum()), "page": 64, "d": 576,

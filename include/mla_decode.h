@@ -63,6 +63,11 @@ extern "C" {
 #define MLA_HEAD_DIM 576
 #define MLA_VALUE_DIM 512
 #define MLA_PAGE_SIZE 64
+/* Element type of q, blocked_k and out (one of the pages lists FP16 beside
+ * BF16; the others BF16 only).  The arithmetic is the same: products of the
+ * 16-bit inputs accumulated in fp32. */
+#define MLA_DTYPE_BF16 0
+#define MLA_DTYPE_FP16 1
 #define MLA_METADATA_WORDS 8   /* int32 words per part in tile_metadata */
 #define MLA_MAX_BATCH 16384
 #define MLA_MAX_ROWS 4096      /* max s_q * h_q / h_kv */
@@ -126,18 +131,20 @@ size_t mla_decode_workspace_size(int batch, int q_rows_per_kv_head, int h_kv, in
 
 /*
  * Call 2: paged MLA decode (the pages' flash_mla_with_kvcache).
- *   q              device bf16 [batch, s_q, h_q, 576], 16-byte aligned
- *   blocked_k      device bf16 [num_pages, 64, h_kv, 576], 16-byte aligned
+ *   q              device [batch, s_q, h_q, 576] of dtype, 16-byte aligned
+ *   blocked_k      device [num_pages, 64, h_kv, 576] of dtype, 16-byte aligned
  *   block_table    device int32 [batch, max_blocks_per_seq]
  *   cache_seqlens  device int32 [batch]
  *   d, dv          must be 576 and 512; page_size must be 64
+ *   dtype          MLA_DTYPE_BF16 or MLA_DTYPE_FP16 (else MLA_ERR_UNSUPPORTED):
+ *                  the element type of q, blocked_k and out
  *   h_q % h_kv == 0; M = s_q * h_q / h_kv <= MLA_MAX_ROWS
  *   tile_metadata, num_parts, num_splits  from mla_get_metadata with
  *                  q_rows_per_kv_head = M and the same h_kv
  *   causal         0/1: query t sees keys j <= N - s_q + t
  *   softmax_scale  multiplies the scores; positive and finite (the usual value
  *                  is 576^-0.5)
- *   out            device bf16 [batch, s_q, h_q, 512], 16-byte aligned,
+ *   out            device [batch, s_q, h_q, 512] of dtype, 16-byte aligned,
  *                  rounded to nearest even
  *   lse            device fp32 [batch, s_q, h_q], natural log
  *   workspace      device, >= mla_decode_workspace_size(batch, M, h_kv,
@@ -147,7 +154,7 @@ size_t mla_decode_workspace_size(int batch, int q_rows_per_kv_head, int h_kv, in
  */
 int mla_decode(const void *q, const void *blocked_k, const int32_t *block_table,
                const int32_t *cache_seqlens, int batch, int s_q, int h_q, int h_kv, int d, int dv,
-               int num_pages, int page_size, int max_blocks_per_seq,
+               int dtype, int num_pages, int page_size, int max_blocks_per_seq,
                const int32_t *tile_metadata, int num_parts, const int32_t *num_splits, int causal,
                float softmax_scale, void *out, float *lse, void *workspace,
                size_t workspace_bytes, void *stream);
@@ -164,18 +171,18 @@ int mla_decode(const void *q, const void *blocked_k, const int32_t *block_table,
  *
  * mla_decode_combine: merges the partials of sequences with several pieces
  * into out/lse (a sequence with one piece is left untouched).  batch, s_q,
- * h_q, h_kv, num_parts, num_splits, workspace and workspace_bytes must be the
+ * h_q, h_kv, num_parts, dtype, num_splits, workspace and workspace_bytes must be the
  * values given to the preceding mla_decode_splitkv.
  */
 int mla_decode_splitkv(const void *q, const void *blocked_k, const int32_t *block_table,
                        const int32_t *cache_seqlens, int batch, int s_q, int h_q, int h_kv,
-                       int d, int dv, int num_pages, int page_size, int max_blocks_per_seq,
+                       int d, int dv, int dtype, int num_pages, int page_size, int max_blocks_per_seq,
                        const int32_t *tile_metadata, int num_parts, const int32_t *num_splits,
                        int causal, float softmax_scale, void *out, float *lse, void *workspace,
                        size_t workspace_bytes, void *stream);
 
 int mla_decode_combine(const int32_t *num_splits, int batch, int s_q, int h_q, int h_kv,
-                       int num_parts, void *out, float *lse, const void *workspace,
+                       int num_parts, int dtype, void *out, float *lse, const void *workspace,
                        size_t workspace_bytes, void *stream);
 
 /* ---- Measurement helpers (not part of the decode path) --------------------

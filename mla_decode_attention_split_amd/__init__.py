@@ -27,6 +27,7 @@ __all__ = [
 
 HEAD_DIM = 576
 VALUE_DIM = 512
+DTYPE_BF16, DTYPE_FP16 = 0, 1  # element types of q, the cache and out (mla_decode.h)
 PAGE_SIZE = 64
 METADATA_WORDS = 8
 
@@ -67,13 +68,13 @@ def _load():
     lib.mla_get_metadata.restype = i
     lib.mla_decode_workspace_size.argtypes = [i, i, i, i]
     lib.mla_decode_workspace_size.restype = sz
-    decode_args = [p, p, p, p, i, i, i, i, i, i, i, i, i, p, i, p, i, ctypes.c_float, p, p, p, sz,
-                   p]
+    decode_args = [p, p, p, p, i, i, i, i, i, i, i, i, i, i, p, i, p, i, ctypes.c_float, p, p, p,
+                   sz, p]
     lib.mla_decode.argtypes = decode_args
     lib.mla_decode.restype = i
     lib.mla_decode_splitkv.argtypes = decode_args
     lib.mla_decode_splitkv.restype = i
-    lib.mla_decode_combine.argtypes = [p, i, i, i, i, i, p, p, p, sz, p]
+    lib.mla_decode_combine.argtypes = [p, i, i, i, i, i, i, p, p, p, sz, p]
     lib.mla_decode_combine.restype = i
     lib.mla_ceiling_stream.argtypes = [p, i, i, p, i, i, p, p]
     lib.mla_ceiling_stream.restype = i
@@ -149,8 +150,10 @@ def mla_decode_workspace_size(batch: int, q_rows_per_kv_head: int, h_kv: int,
 def _decode_call(fn_name, q, blocked_k, block_table, cache_seqlens, tile_metadata, num_splits,
                  causal, softmax_scale, out, lse, workspace):
     import torch
-    if q.dtype != torch.bfloat16 or blocked_k.dtype != torch.bfloat16:
-        raise ValueError("q and blocked_k must be bfloat16")
+    dtypes = {torch.bfloat16: DTYPE_BF16, torch.float16: DTYPE_FP16}
+    if q.dtype not in dtypes or blocked_k.dtype != q.dtype:
+        raise ValueError("q and blocked_k must both be bfloat16 or both float16")
+    dtype = dtypes[q.dtype]
     if block_table.dtype != torch.int32 or cache_seqlens.dtype != torch.int32:
         raise ValueError("block_table and cache_seqlens must be int32")
     if tile_metadata.dtype != torch.int32 or num_splits.dtype != torch.int32:
@@ -178,7 +181,9 @@ def _decode_call(fn_name, q, blocked_k, block_table, cache_seqlens, tile_metadat
     M = s_q * h_q // max(h_kv, 1)
     with torch.cuda.device(dev):
         if out is None:
-            out = torch.empty((B, s_q, h_q, VALUE_DIM), dtype=torch.bfloat16, device=dev)
+            out = torch.empty((B, s_q, h_q, VALUE_DIM), dtype=q.dtype, device=dev)
+        elif out.dtype != q.dtype:
+            raise ValueError("out must have q's dtype")
         if lse is None:
             lse = torch.empty((B, s_q, h_q), dtype=torch.float32, device=dev)
         need = mla_decode_workspace_size(B, M, h_kv, num_parts) if h_q % max(h_kv, 1) == 0 else 0
@@ -186,7 +191,7 @@ def _decode_call(fn_name, q, blocked_k, block_table, cache_seqlens, tile_metadat
             workspace = torch.empty((max(need, 16),), dtype=torch.uint8, device=dev)
         fn = getattr(_load(), fn_name)
         _check(fn(q.data_ptr(), blocked_k.data_ptr(), block_table.data_ptr(),
-                  cache_seqlens.data_ptr(), B, s_q, h_q, h_kv, d, VALUE_DIM, num_pages, page,
+                  cache_seqlens.data_ptr(), B, s_q, h_q, h_kv, d, VALUE_DIM, dtype, num_pages, page,
                   block_table.shape[1], tile_metadata.data_ptr(), num_parts, num_splits.data_ptr(),
                   int(bool(causal)), scale, out.data_ptr(), lse.data_ptr(), workspace.data_ptr(),
                   workspace.numel() * workspace.element_size(), _stream_of(dev)))
@@ -217,10 +222,12 @@ def mla_decode_splitkv(q, blocked_k, block_table, cache_seqlens, tile_metadata, 
 
 def mla_decode_combine(num_splits, out, lse, workspace, *, num_parts: int, h_kv: int = 1):
     """Merge the split partials left by :func:`mla_decode_splitkv`."""
+    import torch
     B, s_q, h_q, _ = out.shape
+    dtype = {torch.bfloat16: DTYPE_BF16, torch.float16: DTYPE_FP16}[out.dtype]
     with _torch_device(out.device):
         _check(_load().mla_decode_combine(
-            num_splits.data_ptr(), B, s_q, h_q, int(h_kv), int(num_parts), out.data_ptr(),
+            num_splits.data_ptr(), B, s_q, h_q, int(h_kv), int(num_parts), dtype, out.data_ptr(),
             lse.data_ptr(), workspace.data_ptr(), workspace.numel() * workspace.element_size(),
             _stream_of(out.device)))
     return out, lse

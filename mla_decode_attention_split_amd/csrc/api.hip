@@ -137,7 +137,7 @@ namespace {
 // Shared checks and argument packing of mla_decode / mla_decode_splitkv.
 int prepare_decode(const void* q, const void* blocked_k, const int32_t* block_table,
                    const int32_t* cache_seqlens, int batch, int s_q, int h_q, int h_kv, int d,
-                   int dv, int num_pages, int page_size, int max_blocks_per_seq,
+                   int dv, int dtype, int num_pages, int page_size, int max_blocks_per_seq,
                    const int32_t* tile_metadata, int num_parts, const int32_t* num_splits,
                    int causal, float softmax_scale, void* out, float* lse, void* workspace,
                    size_t workspace_bytes, mla::DecodeArgs* a, int* tile_rows) {
@@ -146,6 +146,8 @@ int prepare_decode(const void* q, const void* blocked_k, const int32_t* block_ta
     return fail(MLA_ERR_UNSUPPORTED, "value dim %d (only %d)", dv, MLA_VALUE_DIM);
   if (page_size != MLA_PAGE_SIZE)
     return fail(MLA_ERR_UNSUPPORTED, "page size %d (only %d)", page_size, MLA_PAGE_SIZE);
+  if (dtype != MLA_DTYPE_BF16 && dtype != MLA_DTYPE_FP16)
+    return fail(MLA_ERR_UNSUPPORTED, "dtype %d (only MLA_DTYPE_BF16 or MLA_DTYPE_FP16)", dtype);
   if (batch < 1 || batch > MLA_MAX_BATCH)
     return fail(MLA_ERR_INVALID_ARG, "batch %d outside [1, %d]", batch, MLA_MAX_BATCH);
   if (s_q < 1 || h_q < 1 || h_kv < 1 || h_q % h_kv != 0)
@@ -203,6 +205,7 @@ int prepare_decode(const void* q, const void* blocked_k, const int32_t* block_ta
   a->causal = causal ? 1 : 0;
   a->xcd_map = (num_parts % 8 == 0) ? 1 : 0;
   a->scale_log2 = softmax_scale * 1.44269504088896340736f;
+  a->f16 = dtype == MLA_DTYPE_FP16 ? 1 : 0;
   const long long grid = (long long)num_parts * a->m_tiles * h_kv;
   if (grid > 0x7fffffffLL) return fail(MLA_ERR_UNSUPPORTED, "grid too large");
   *tile_rows = tr;
@@ -221,6 +224,7 @@ int enqueue_combine(const mla::DecodeArgs& a, hipStream_t st) {
   c.h_q = a.h_q;
   c.h_kv = a.h_kv;
   c.M = a.M;
+  c.f16 = a.f16;
   c.share_grid = 0;
   hipError_t e = mla::launch_combine(c, a.num_parts, st);
   if (e != hipSuccess) return fail(MLA_ERR_HIP, "combine launch: %s", hipGetErrorString(e));
@@ -231,14 +235,14 @@ int enqueue_combine(const mla::DecodeArgs& a, hipStream_t st) {
 
 int mla_decode_splitkv(const void* q, const void* blocked_k, const int32_t* block_table,
                        const int32_t* cache_seqlens, int batch, int s_q, int h_q, int h_kv,
-                       int d, int dv, int num_pages, int page_size, int max_blocks_per_seq,
+                       int d, int dv, int dtype, int num_pages, int page_size, int max_blocks_per_seq,
                        const int32_t* tile_metadata, int num_parts, const int32_t* num_splits,
                        int causal, float softmax_scale, void* out, float* lse, void* workspace,
                        size_t workspace_bytes, void* stream) {
   mla::DecodeArgs a;
   int tr = 0;
   int rc = prepare_decode(q, blocked_k, block_table, cache_seqlens, batch, s_q, h_q, h_kv, d, dv,
-                          num_pages, page_size, max_blocks_per_seq, tile_metadata, num_parts,
+                          dtype, num_pages, page_size, max_blocks_per_seq, tile_metadata, num_parts,
                           num_splits, causal, softmax_scale, out, lse, workspace,
                           workspace_bytes, &a, &tr);
   if (rc != MLA_OK) return rc;
@@ -248,7 +252,7 @@ int mla_decode_splitkv(const void* q, const void* blocked_k, const int32_t* bloc
 }
 
 int mla_decode_combine(const int32_t* num_splits, int batch, int s_q, int h_q, int h_kv,
-                       int num_parts, void* out, float* lse, const void* workspace,
+                       int num_parts, int dtype, void* out, float* lse, const void* workspace,
                        size_t workspace_bytes, void* stream) {
   if (batch < 1 || batch > MLA_MAX_BATCH)
     return fail(MLA_ERR_INVALID_ARG, "batch %d outside [1, %d]", batch, MLA_MAX_BATCH);
@@ -260,6 +264,8 @@ int mla_decode_combine(const int32_t* num_splits, int batch, int s_q, int h_q, i
     return fail(MLA_ERR_UNSUPPORTED, "s_q * h_q / h_kv = %lld > %d", M_ll, MLA_MAX_ROWS);
   if (num_parts < 1 || num_parts > MLA_MAX_PARTS)
     return fail(MLA_ERR_INVALID_ARG, "num_parts %d outside [1, %d]", num_parts, MLA_MAX_PARTS);
+  if (dtype != MLA_DTYPE_BF16 && dtype != MLA_DTYPE_FP16)
+    return fail(MLA_ERR_UNSUPPORTED, "dtype %d (only MLA_DTYPE_BF16 or MLA_DTYPE_FP16)", dtype);
   if (!num_splits || !out || !lse || !workspace)
     return fail(MLA_ERR_INVALID_ARG, "null pointer argument");
   if (!aligned16(out) || !aligned16(workspace))
@@ -282,6 +288,7 @@ int mla_decode_combine(const int32_t* num_splits, int batch, int s_q, int h_q, i
   a.h_kv = h_kv;
   a.M = M;
   a.num_parts = num_parts;
+  a.f16 = dtype == MLA_DTYPE_FP16 ? 1 : 0;
   int rc = enqueue_combine(a, static_cast<hipStream_t>(stream));
   if (rc != MLA_OK) return rc;
   return ok();
@@ -289,14 +296,14 @@ int mla_decode_combine(const int32_t* num_splits, int batch, int s_q, int h_q, i
 
 int mla_decode(const void* q, const void* blocked_k, const int32_t* block_table,
                const int32_t* cache_seqlens, int batch, int s_q, int h_q, int h_kv, int d, int dv,
-               int num_pages, int page_size, int max_blocks_per_seq,
+               int dtype, int num_pages, int page_size, int max_blocks_per_seq,
                const int32_t* tile_metadata, int num_parts, const int32_t* num_splits, int causal,
                float softmax_scale, void* out, float* lse, void* workspace,
                size_t workspace_bytes, void* stream) {
   mla::DecodeArgs a;
   int tr = 0;
   int rc = prepare_decode(q, blocked_k, block_table, cache_seqlens, batch, s_q, h_q, h_kv, d, dv,
-                          num_pages, page_size, max_blocks_per_seq, tile_metadata, num_parts,
+                          dtype, num_pages, page_size, max_blocks_per_seq, tile_metadata, num_parts,
                           num_splits, causal, softmax_scale, out, lse, workspace,
                           workspace_bytes, &a, &tr);
   if (rc != MLA_OK) return rc;

@@ -141,10 +141,17 @@ __global__ __launch_bounds__(64 * kCombineWaves) void combine_kernel(CombineArgs
   const int h = g * hpg + m % hpg;
   const long long out_row = ((long long)b * a.s_q + t) * a.h_q + h;
   uint4 pk;
-  pk.x = pack_bf16(acc[0], acc[1]);
-  pk.y = pack_bf16(acc[2], acc[3]);
-  pk.z = pack_bf16(acc[4], acc[5]);
-  pk.w = pack_bf16(acc[6], acc[7]);
+  if (a.f16) {
+    pk.x = pack_f16(acc[0], acc[1]);
+    pk.y = pack_f16(acc[2], acc[3]);
+    pk.z = pack_f16(acc[4], acc[5]);
+    pk.w = pack_f16(acc[6], acc[7]);
+  } else {
+    pk.x = pack_bf16(acc[0], acc[1]);
+    pk.y = pack_bf16(acc[2], acc[3]);
+    pk.z = pack_bf16(acc[4], acc[5]);
+    pk.w = pack_bf16(acc[6], acc[7]);
+  }
   *reinterpret_cast<uint4*>(a.out + out_row * kValueDim + lane * 8) = pk;
   if (lane == 0) a.lse[out_row] = L;
 }

@@ -88,14 +88,6 @@ __device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t r, unsigned vo
                                            char MLA_LDS* dst) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (void MLA_LDS*)dst, 16, voff, 0, 0, 0);
 }
-__device__ __forceinline__ f32x16 mfma32(i16x8 a, i16x8 b, f32x16 c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
-                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
-}
-__device__ __forceinline__ f32x4 mfma16(i16x8 a, i16x8 b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
-                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
-}
 __device__ __forceinline__ int readlane(int v, int lane) { return __builtin_amdgcn_readlane(v, lane); }
 // max of x over lanes l and l ^ 32 (v_permlane32_swap), and l ^ 16
 __device__ __forceinline__ float max_xor32(float x) {
@@ -160,7 +152,7 @@ struct Tile {
   static_assert(kLdsBytes + XCH_BUFS * XCH_ONE <= 163840, "LDS capacity");
 };
 
-template <int R, int RG, int DG, bool QG>
+template <int R, int RG, int DG, bool QG, typename E>
 __global__ __launch_bounds__(256, 1) void decode_kernel(
     const uint16_t* __restrict__ q_ptr, const uint16_t* __restrict__ kv_ptr,
     const int32_t* __restrict__ block_table, const int32_t* __restrict__ seqlens,
@@ -525,15 +517,14 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(
         st.rsum = 0.f;
       } else if (slice < kSoftSlices) {
         const int e0 = 4 * (slice - 3);
-        const bf16x2 ones = __builtin_bit_cast(bf16x2, 0x3f803f80u);
 #pragma unroll
         for (int i = 0; i < 4; i += 2) {
           const float p0 = fast_exp2(__builtin_fmaf(x[e0 + i], a.scale_log2, -m_run));
           const float p1 = fast_exp2(__builtin_fmaf(x[e0 + i + 1], a.scale_log2, -m_run));
-          const uint32_t pk = pack_bf16(p0, p1);
+          const uint32_t pk = E::pack(p0, p1);
           st.pw[(e0 + i) >> 1] = pk;
           st.sum += p0 + p1;
-          st.rsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk), ones, st.rsum, false);
+          st.rsum = E::dot2(pk, E::kOnePair, st.rsum);
         }
         if (slice == kSoftSlices - 1) {
           l_run += st.sum;
@@ -569,7 +560,7 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(
 #pragma unroll
         for (int idx = 0; idx < NV; ++idx) {
           const int kb = idx / NT, nt = idx % NT;
-          o[nt] = mfma32(va[idx % VP], pb[kb], o[nt]);
+          o[nt] = E::mfma32(va[idx % VP], pb[kb], o[nt]);
           if (idx + VP < NV) va[idx % VP] = vread(idx + VP);
           if (first_slot >= 0) fire_slot(first_slot + idx);
           __builtin_amdgcn_sched_barrier(0);
@@ -587,7 +578,7 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(
         for (int j2 = 0; j2 < VP; ++j2) va[j2] = vread(j2);
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
-          o[nt] = mfma16(va[nt % VP], pb, o[nt]);
+          o[nt] = E::mfma16(va[nt % VP], pb, o[nt]);
           if (nt + VP < NT) va[nt % VP] = vread(nt + VP);
           if (first_slot >= 0) fire_slot(first_slot + nt);
           __builtin_amdgcn_sched_barrier(0);
@@ -666,8 +657,8 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int i = 0; i < NK; ++i) {
-          if constexpr (R == 32) sacc[0] = mfma32(kf[i % KP], qf[i], sacc[0]);
-          else sacc[i % KB_W] = mfma16(kf[i % KP], qf[i / KB_W], sacc[i % KB_W]);
+          if constexpr (R == 32) sacc[0] = E::mfma32(kf[i % KP], qf[i], sacc[0]);
+          else sacc[i % KB_W] = E::mfma16(kf[i % KP], qf[i / KB_W], sacc[i % KB_W]);
           if (i + KP < NK) kf[i % KP] = lds_read_b128(kaddr(i + KP));
           fire_slot(i);
           if constexpr (HP) soft_slice(x, ss, i);
@@ -755,8 +746,8 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(
 #pragma unroll
           for (int qd = 0; qd < QUADS; ++qd) {
             uint2 pk;
-            pk.x = pack_bf16((o[nt][4 * qd + 0]) * inv, (o[nt][4 * qd + 1]) * inv);
-            pk.y = pack_bf16((o[nt][4 * qd + 2]) * inv, (o[nt][4 * qd + 3]) * inv);
+            pk.x = E::pack((o[nt][4 * qd + 0]) * inv, (o[nt][4 * qd + 1]) * inv);
+            pk.y = E::pack((o[nt][4 * qd + 2]) * inv, (o[nt][4 * qd + 3]) * inv);
             *reinterpret_cast<uint2*>(orow + dim_of(nt, qd)) = pk;
           }
         }
@@ -784,33 +775,41 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(
   const uint16_t* __restrict__, const uint16_t* __restrict__, const int32_t* __restrict__,  \
       const int32_t* __restrict__, const int32_t* __restrict__, uint16_t* __restrict__,      \
       float* __restrict__, float* __restrict__, float* __restrict__, DecodeArgs
-template __global__ void decode_kernel<16, 1, 4, false>(MLA_DECODE_PARAMS);
-template __global__ void decode_kernel<16, 2, 2, false>(MLA_DECODE_PARAMS);
-template __global__ void decode_kernel<32, 2, 2, false>(MLA_DECODE_PARAMS);
-template __global__ void decode_kernel<16, 1, 4, true>(MLA_DECODE_PARAMS);
-template __global__ void decode_kernel<16, 2, 2, true>(MLA_DECODE_PARAMS);
-template __global__ void decode_kernel<32, 2, 2, true>(MLA_DECODE_PARAMS);
+#define MLA_DECODE_INSTANCES(E)                                                      \
+  template __global__ void decode_kernel<16, 1, 4, false, E>(MLA_DECODE_PARAMS);   \
+  template __global__ void decode_kernel<16, 2, 2, false, E>(MLA_DECODE_PARAMS);   \
+  template __global__ void decode_kernel<32, 2, 2, false, E>(MLA_DECODE_PARAMS);   \
+  template __global__ void decode_kernel<16, 1, 4, true, E>(MLA_DECODE_PARAMS);    \
+  template __global__ void decode_kernel<16, 2, 2, true, E>(MLA_DECODE_PARAMS);    \
+  template __global__ void decode_kernel<32, 2, 2, true, E>(MLA_DECODE_PARAMS);
+MLA_DECODE_INSTANCES(Bf16)
+MLA_DECODE_INSTANCES(F16)
 
-template <int R, int RG, int DG, bool QG>
+template <int R, int RG, int DG, bool QG, typename E>
 static hipError_t launch_t(const DecodeArgs& a, hipStream_t stream) {
   const int grid = a.num_parts * a.m_tiles * a.h_kv;
-  hipLaunchKernelGGL((decode_kernel<R, RG, DG, QG>), dim3(grid), dim3(256), 0, stream, a.q, a.kv,
+  hipLaunchKernelGGL((decode_kernel<R, RG, DG, QG, E>), dim3(grid), dim3(256), 0, stream, a.q, a.kv,
                      a.block_table, a.seqlens, a.meta, a.out, a.lse, a.o_part, a.lse_part, a);
   return hipGetLastError();
 }
 
-template <bool QG>
+template <bool QG, typename E>
 static hipError_t launch_q(const DecodeArgs& a, int tile_rows, hipStream_t stream) {
   switch (tile_rows) {
-    case 16: return launch_t<16, 1, 4, QG>(a, stream);
-    case 32: return launch_t<16, 2, 2, QG>(a, stream);
-    case 64: return launch_t<32, 2, 2, QG>(a, stream);
+    case 16: return launch_t<16, 1, 4, QG, E>(a, stream);
+    case 32: return launch_t<16, 2, 2, QG, E>(a, stream);
+    case 64: return launch_t<32, 2, 2, QG, E>(a, stream);
     default: return hipErrorInvalidValue;
   }
 }
 
+template <typename E>
+static hipError_t launch_e(const DecodeArgs& a, int tile_rows, hipStream_t stream) {
+  return a.h_kv == 1 ? launch_q<false, E>(a, tile_rows, stream) : launch_q<true, E>(a, tile_rows, stream);
+}
+
 hipError_t launch_decode(const DecodeArgs& a, int tile_rows, hipStream_t stream) {
-  return a.h_kv == 1 ? launch_q<false>(a, tile_rows, stream) : launch_q<true>(a, tile_rows, stream);
+  return a.f16 ? launch_e<F16>(a, tile_rows, stream) : launch_e<Bf16>(a, tile_rows, stream);
 }
 
 }  // namespace mla

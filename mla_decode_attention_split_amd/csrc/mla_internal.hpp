@@ -9,13 +9,13 @@ namespace mla {
 constexpr int kMaxBatch = 16384;  // sequences per call (scheduler keeps prefix costs in LDS)
 
 struct DecodeArgs {
-  const uint16_t* q;          // bf16 [batch, s_q, h_q, 576]
-  const uint16_t* kv;         // bf16 [num_pages, 64, h_kv, 576]
+  const uint16_t* q;          // bf16 or fp16 [batch, s_q, h_q, 576]
+  const uint16_t* kv;         // same type, [num_pages, 64, h_kv, 576]
   const int32_t* block_table; // [batch, max_blocks]
   const int32_t* seqlens;     // [batch]
   const int32_t* meta;        // [num_parts, 8]
   const int32_t* num_splits;  // [batch + 1]
-  uint16_t* out;              // bf16 [batch, s_q, h_q, 512]
+  uint16_t* out;              // q's type, [batch, s_q, h_q, 512]
   float* lse;                 // [batch, s_q, h_q]
   float* o_part;              // [max_pieces, h_kv, M, 512]
   float* lse_part;            // [max_pieces, h_kv, M]
@@ -23,6 +23,7 @@ struct DecodeArgs {
   int causal;
   int xcd_map;                // 1: the m-tiles / KV heads of one part share an XCD
   float scale_log2;           // softmax_scale * log2(e)
+  int f16;                    // 1: q, cache and out are fp16; 0: bf16
 };
 
 struct CombineArgs {
@@ -33,6 +34,7 @@ struct CombineArgs {
   float* lse;
   int batch, s_q, h_q, h_kv, M;
   int share_grid;  // 1: one workgroup per query row (set when sequences have many pieces)
+  int f16;         // 1: out is fp16; 0: bf16
 };
 
 // Query rows per workgroup for M rows per KV head (16, 32 or 64; larger M

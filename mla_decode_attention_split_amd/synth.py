@@ -2,7 +2,7 @@
 
 This module only draws random numbers and lays them out; it holds none of
 the attention arithmetic.  Both the HIP path and the CPU oracle consume what
-it produces (bf16 values are carried as their uint16 bit patterns).
+it produces (bf16 or fp16 values are carried as their uint16 bit patterns).
 
 Shapes follow the pages' call (q, blocked_k, block_table, cache_seqlens) and
 their fixed sizes: row width 576 = 512 latent + 64 rope, page of 64 tokens,
@@ -16,8 +16,11 @@ bf16 storage.  The named workloads are:
 * ``ragged``   B=16, s_q=1, h_q=64, N = clip(rint(lognormal(ln 2048, 1)),
                1, 32768) with N[0] = N[8] = 32768.
 
+* ``hkv2``     B=32, s_q=1, h_q=32, h_kv=2, every N=4096.
+
 Values: q and every cache page (used or not) are N(0, 1) drawn in float32
-and rounded to bf16 (round to nearest even).  block_table is a seeded
+and rounded to bf16 (or, with ``dtype="fp16"``, to fp16), round to nearest
+even.  block_table is a seeded
 permutation of the pool laid out row-major over the pages each sequence
 needs; unused table entries point at ``pad_page``.
 """
@@ -31,6 +34,7 @@ D = 576
 DV = 512
 PAGE = 64
 BF16_NAN = np.uint16(0x7FC0)
+F16_NAN = np.uint16(0x7E00)
 
 WORKLOADS = ("tiny", "membound", "mtp", "large", "ragged", "hkv2")
 
@@ -48,12 +52,14 @@ def bf16_to_f32(bits: np.ndarray) -> np.ndarray:
         np.float32)
 
 
-def _normal_bf16(rng: np.random.Generator, shape, chunk: int = 1 << 24) -> np.ndarray:
+def _normal_16bit(rng: np.random.Generator, shape, chunk: int = 1 << 24,
+                 dtype: str = "bf16") -> np.ndarray:
     n = int(np.prod(shape))
     out = np.empty(n, dtype=np.uint16)
     for s in range(0, n, chunk):
         e = min(n, s + chunk)
-        out[s:e] = bf16_bits(rng.standard_normal(e - s, dtype=np.float32))
+        x = rng.standard_normal(e - s, dtype=np.float32)
+        out[s:e] = bf16_bits(x) if dtype == "bf16" else x.astype(np.float16).view(np.uint16)
     return out.reshape(shape)
 
 
@@ -70,6 +76,7 @@ class Workload:
     causal: bool
     scale: float
     meta: dict = field(default_factory=dict)
+    dtype: str = "bf16"      # element type of q and kcache: "bf16" or "fp16"
 
     @property
     def batch(self) -> int:
@@ -83,7 +90,7 @@ class Workload:
 def make_workload(seqlens, *, s_q: int = 1, h_q: int = 16, h_kv: int = 1, causal: bool = False,
                   seed: int = 0, extra_pages: int = 0, table_width: int | None = None,
                   pad: str = "valid", poison_tail: bool = False, name: str = "custom",
-                  scale: float | None = None) -> Workload:
+                  scale: float | None = None, dtype: str = "bf16") -> Workload:
     """Paged workload for the given sequence lengths.
 
     ``pad``: what unused block_table entries hold -- ``"valid"`` (page 0 of
@@ -102,8 +109,11 @@ def make_workload(seqlens, *, s_q: int = 1, h_q: int = 16, h_kv: int = 1, causal
     if width < (pages_needed.max() if B else 0):
         raise ValueError("table_width smaller than the pages a sequence needs")
     perm = rng.permutation(pool).astype(np.int32)
-    q = _normal_bf16(rng, (B, s_q, h_q, D))
-    kcache = _normal_bf16(rng, (pool + (1 if pad == "poison" else 0), PAGE, h_kv, D))
+    if dtype not in ("bf16", "fp16"):
+        raise ValueError("dtype must be bf16 or fp16")
+    nan = BF16_NAN if dtype == "bf16" else F16_NAN
+    q = _normal_16bit(rng, (B, s_q, h_q, D), dtype=dtype)
+    kcache = _normal_16bit(rng, (pool + (1 if pad == "poison" else 0), PAGE, h_kv, D), dtype=dtype)
     pad_val = {"valid": 0, "poison": pool, "minus1": -1}[pad]
     table = np.full((B, width), pad_val, dtype=np.int32)
     off = 0
@@ -112,47 +122,51 @@ def make_workload(seqlens, *, s_q: int = 1, h_q: int = 16, h_kv: int = 1, causal
         table[b, :r] = perm[off:off + r]
         off += r
     if pad == "poison":
-        kcache[pool] = BF16_NAN
+        kcache[pool] = nan
     if poison_tail:
         for b in range(B):
             n = int(seqlens[b])
             if n % PAGE:
-                kcache[table[b, n // PAGE], n % PAGE:] = BF16_NAN
+                kcache[table[b, n // PAGE], n % PAGE:] = nan
         for p in perm[used:]:
-            kcache[p] = BF16_NAN
+            kcache[p] = nan
     return Workload(name=name, q=q, kcache=kcache, block_table=table, seqlens=seqlens, s_q=s_q,
                     h_q=h_q, h_kv=h_kv, causal=causal,
                     scale=float(D ** -0.5) if scale is None else float(scale),
-                    meta={"seed": seed, "pool_pages": pool})
+                    meta={"seed": seed, "pool_pages": pool}, dtype=dtype)
 
 
-def named_workload(name: str, seed: int | None = None) -> Workload:
-    """One of the named workloads (seed defaults to its index)."""
+def named_workload(name: str, seed: int | None = None, dtype: str = "bf16") -> Workload:
+    """One of the named workloads (seed defaults to its index); ``dtype``
+    "fp16" draws the same shapes in fp16 (tiny is bf16 only)."""
     idx = WORKLOADS.index(name)
     seed = idx if seed is None else seed
+    kw = {"dtype": dtype}
     if name == "tiny":
+        if dtype != "bf16":
+            raise ValueError("the tiny workload is bf16 only")
         rng = np.random.default_rng(seed)
         perm = rng.permutation(8).astype(np.int32)
-        q = _normal_bf16(rng, (2, 1, 16, D))
-        kcache = _normal_bf16(rng, (8, PAGE, 1, D))
+        q = _normal_16bit(rng, (2, 1, 16, D))
+        kcache = _normal_16bit(rng, (8, PAGE, 1, D))
         return Workload(name=name, q=q, kcache=kcache, block_table=perm.reshape(2, 4).copy(),
                         seqlens=np.array([64, 200], dtype=np.int32), s_q=1, h_q=16, h_kv=1,
                         causal=False, scale=float(D ** -0.5), meta={"seed": seed, "pool_pages": 8})
     if name == "membound":
-        return make_workload(np.full(32, 4096), s_q=1, h_q=16, seed=seed, name=name)
+        return make_workload(np.full(32, 4096), s_q=1, h_q=16, seed=seed, name=name, **kw)
     if name == "mtp":
         rng = np.random.default_rng(1000 + seed)
         lens = rng.integers(1024, 8193, size=64)
-        return make_workload(lens, s_q=2, h_q=128, causal=True, seed=seed, name=name)
+        return make_workload(lens, s_q=2, h_q=128, causal=True, seed=seed, name=name, **kw)
     if name == "large":
-        return make_workload(np.full(128, 4096), s_q=1, h_q=128, seed=seed, name=name)
+        return make_workload(np.full(128, 4096), s_q=1, h_q=128, seed=seed, name=name, **kw)
     if name == "ragged":
         rng = np.random.default_rng(1000 + seed)
         lens = np.clip(np.rint(rng.lognormal(np.log(2048.0), 1.0, size=16)), 1, 32768)
         lens[0] = 32768
         lens[8] = 32768
-        return make_workload(lens.astype(np.int32), s_q=1, h_q=64, seed=seed, name=name)
+        return make_workload(lens.astype(np.int32), s_q=1, h_q=64, seed=seed, name=name, **kw)
     if name == "hkv2":  # two latent KV heads, 16 query heads each
-        return make_workload(np.full(32, 4096), s_q=1, h_q=32, h_kv=2, seed=seed, name=name)
+        return make_workload(np.full(32, 4096), s_q=1, h_q=32, h_kv=2, seed=seed, name=name, **kw)
     raise KeyError(name)
 

@@ -64,10 +64,12 @@ def _load():
         p = ctypes.c_void_p
         i = ctypes.c_int
         lib.mla_oracle_decode.argtypes = [p, p, p, p, i, i, i, i, i, i, i, i, i, i,
-                                          ctypes.c_double, p, p]
+                                          ctypes.c_double, i, p, p]
         lib.mla_oracle_decode.restype = i
         lib.mla_oracle_decode_split.argtypes = [p, p, p, p, i, i, i, i, i, i, i, i, i, i,
-                                                ctypes.c_double, p, p, p, p]
+                                                ctypes.c_double, i, p, p, p, p]
+        lib.mla_oracle_widen.argtypes = [p, ctypes.c_long, i, p]
+        lib.mla_oracle_widen.restype = i
         lib.mla_oracle_decode_split.restype = i
         lib.mla_oracle_schedule.argtypes = [p, i, i, i, i, p, p]
         lib.mla_oracle_schedule.restype = i
@@ -100,11 +102,25 @@ def _prep(q, kcache, block_table, seqlens):
     return q, kcache, block_table, seqlens, (B, s_q, h_q, d, num_pages, page, h_kv)
 
 
-def decode(q, kcache, block_table, seqlens, *, causal: bool, scale: float, dv: int = DV):
+_DTYPES = {"bf16": 0, "fp16": 1}
+
+
+def widen(bits, dtype: str = "bf16"):
+    """The float64 values of 16-bit bit patterns (uint16) of type ``dtype``."""
+    bits = np.ascontiguousarray(bits, dtype=np.uint16)
+    out = np.zeros(bits.shape, dtype=np.float64)
+    rc = _load().mla_oracle_widen(_ptr(bits), int(bits.size), _DTYPES[dtype], _ptr(out))
+    if rc != 0:
+        raise ValueError(f"mla_oracle_widen failed with code {rc}")
+    return out
+
+
+def decode(q, kcache, block_table, seqlens, *, causal: bool, scale: float, dv: int = DV,
+           dtype: str = "bf16"):
     """Reference decode in float64.
 
-    ``q``: bf16 bits uint16 [B, s_q, h_q, d]; ``kcache``: bf16 bits uint16
-    [num_pages, page, h_kv, d]; ``block_table``: int32 [B, max_blocks];
+    ``q``: 16-bit bits uint16 [B, s_q, h_q, d] of type ``dtype`` ("bf16" or
+    "fp16"); ``kcache``: same type, uint16 [num_pages, page, h_kv, d]; ``block_table``: int32 [B, max_blocks];
     ``seqlens``: int32 [B].  Returns ``(out [B, s_q, h_q, dv] float64,
     lse [B, s_q, h_q] float64)``; empty rows give out 0 and lse -inf.
     """
@@ -114,14 +130,14 @@ def decode(q, kcache, block_table, seqlens, *, causal: bool, scale: float, dv: i
     lse = np.zeros((B, s_q, h_q), dtype=np.float64)
     rc = _load().mla_oracle_decode(_ptr(q), _ptr(kcache), _ptr(block_table), _ptr(seqlens), B, s_q,
                                    h_q, h_kv, d, dv, page, P, block_table.shape[1], int(causal),
-                                   float(scale), _ptr(out), _ptr(lse))
+                                   float(scale), _DTYPES[dtype], _ptr(out), _ptr(lse))
     if rc != 0:
         raise ValueError(f"mla_oracle_decode failed with code {rc}")
     return out, lse
 
 
 def decode_split(q, kcache, block_table, seqlens, cuts, *, causal: bool, scale: float,
-                 dv: int = DV):
+                 dv: int = DV, dtype: str = "bf16"):
     """Piecewise decode merged by log-sum-exp.
 
     ``cuts``: list (length B) of ascending interior cut positions (token
@@ -141,7 +157,8 @@ def decode_split(q, kcache, block_table, seqlens, cuts, *, causal: bool, scale: 
     lse = np.zeros((B, s_q, h_q), dtype=np.float64)
     rc = _load().mla_oracle_decode_split(_ptr(q), _ptr(kcache), _ptr(block_table), _ptr(seqlens),
                                          B, s_q, h_q, h_kv, d, dv, page, P, block_table.shape[1],
-                                         int(causal), float(scale), _ptr(cut_ptr), _ptr(flat),
+                                         int(causal), float(scale), _DTYPES[dtype], _ptr(cut_ptr),
+                                         _ptr(flat),
                                          _ptr(out), _ptr(lse))
     if rc != 0:
         raise ValueError(f"mla_oracle_decode_split failed with code {rc}")

@@ -6,8 +6,9 @@
  * baseline leg use it.  It shares no code, header, table or constant with the
  * HIP library; both sides only share the seeded input generator.
  *
- * Plain, slow, obviously correct.  Inputs are bf16 bit patterns (widened to
- * double exactly); every sum, exp and log is done in double precision.
+ * Plain, slow, obviously correct.  Inputs are bf16 or fp16 bit patterns
+ * (widened to double exactly); every sum, exp and log is done in double
+ * precision.
  *
  * What is computed (sources: the pages on FlashMLA):
  *   - "DeepSeek 开源记-第1天-FlashMLA" (cnblogs), section 2 "核心功能": head
@@ -19,6 +20,8 @@
  *     tile_scheduler_metadata, num_splits, causal) and the (output, lse) pair.
  *   - "DeepSeek代碼開源第一彈Flash MLA" (ygpos news): BF16, paged KV cache with
  *     block size 64, variable-length sequences.
+ *   - "什么是FlashMLA" (jsxs2.com), section on supported precisions: FP16
+ *     beside BF16.
  *   - FlashMLA explainer (jsxs2.com), section 3.1 "分块调度与并行计算": the work
  *     is cut into small blocks that run in parallel (the split scheduler).
  *
@@ -45,12 +48,41 @@
 #define ORACLE_ERR_PAGE (-2)
 #define ORACLE_ERR_NOMEM (-3)
 
+#define ORACLE_BF16 0
+#define ORACLE_FP16 1
+
 /* bf16 is the upper half of an IEEE binary32; widening is exact. */
 static double bf16_to_double(uint16_t bits) {
   uint32_t u = ((uint32_t)bits) << 16;
   float f;
   memcpy(&f, &u, sizeof f);
   return (double)f;
+}
+
+/* IEEE 754 binary16: 1 sign bit, 5 exponent bits (bias 15), 10 fraction
+ * bits.  Exponent 0 holds zero and the subnormals f * 2^-24; exponent 31
+ * holds infinities (f = 0) and NaNs.  Every value is exact in double. */
+static double fp16_to_double(uint16_t bits) {
+  const int sign = bits >> 15, e = (bits >> 10) & 31, f = bits & 1023;
+  double v;
+  if (e == 0)
+    v = ldexp((double)f, -24);
+  else if (e == 31)
+    v = f ? NAN : INFINITY;
+  else
+    v = ldexp((double)(1024 + f), e - 25); /* (1 + f/1024) * 2^(e-15) */
+  return sign ? -v : v;
+}
+
+static double widen(uint16_t bits, int dtype) {
+  return dtype == ORACLE_FP16 ? fp16_to_double(bits) : bf16_to_double(bits);
+}
+
+/* Widen n bit patterns of the given type (0 bf16, 1 fp16) to double. */
+int mla_oracle_widen(const uint16_t *bits, long n, int dtype, double *out) {
+  if (!bits || !out || n < 0 || (dtype != ORACLE_BF16 && dtype != ORACLE_FP16)) return ORACLE_ERR_ARG;
+  for (long i = 0; i < n; ++i) out[i] = widen(bits[i], dtype);
+  return ORACLE_OK;
 }
 
 int mla_oracle_num_threads(void) {
@@ -99,11 +131,11 @@ static int check_args(const int32_t *block_table, const int32_t *seqlens, int B,
 /* Scaled score of every key j in [0, n_keys) for one query row. */
 static void row_scores(const uint16_t *qrow, const uint16_t *kcache, const int32_t *block_table,
                        int b, int g, long n_keys, int h_kv, int d, int page_size, int max_blocks,
-                       double scale, double *s) {
+                       double scale, int dtype, double *s) {
   for (long j = 0; j < n_keys; ++j) {
     const uint16_t *k = key_row(kcache, block_table, b, j, g, h_kv, d, page_size, max_blocks);
     double acc = 0.0;
-    for (int c = 0; c < d; ++c) acc += bf16_to_double(qrow[c]) * bf16_to_double(k[c]);
+    for (int c = 0; c < d; ++c) acc += widen(qrow[c], dtype) * widen(k[c], dtype);
     s[j] = scale * acc;
   }
 }
@@ -113,7 +145,7 @@ static void row_scores(const uint16_t *qrow, const uint16_t *kcache, const int32
  * An empty piece gives lse = -inf and out = 0. */
 static void attend_range(const double *s, long j0, long j1, const uint16_t *kcache,
                          const int32_t *block_table, int b, int g, int h_kv, int d, int dv,
-                         int page_size, int max_blocks, double *out, double *lse) {
+                         int page_size, int max_blocks, int dtype, double *out, double *lse) {
   for (int v = 0; v < dv; ++v) out[v] = 0.0;
   if (j1 <= j0) {
     *lse = -INFINITY;
@@ -128,13 +160,14 @@ static void attend_range(const double *s, long j0, long j1, const uint16_t *kcac
   for (long j = j0; j < j1; ++j) {
     double w = exp(s[j] - l);
     const uint16_t *k = key_row(kcache, block_table, b, j, g, h_kv, d, page_size, max_blocks);
-    for (int v = 0; v < dv; ++v) out[v] += w * bf16_to_double(k[v]);
+    for (int v = 0; v < dv; ++v) out[v] += w * widen(k[v], dtype);
   }
   *lse = l;
 }
 
 /*
- * Reference decode.  Layouts (row-major, bf16 as uint16 bit patterns):
+ * Reference decode.  Layouts (row-major, 16-bit bit patterns as uint16 of
+ * type dtype: 0 bf16, 1 fp16):
  *   q           [B, s_q, h_q, d]
  *   kcache      [num_pages, page_size, h_kv, d]
  *   block_table [B, max_blocks]   physical page of logical block i of sequence b
@@ -146,7 +179,8 @@ static void attend_range(const double *s, long j0, long j1, const uint16_t *kcac
 int mla_oracle_decode(const uint16_t *q, const uint16_t *kcache, const int32_t *block_table,
                       const int32_t *seqlens, int B, int s_q, int h_q, int h_kv, int d, int dv,
                       int page_size, int num_pages, int max_blocks, int causal, double scale,
-                      double *out, double *lse) {
+                      int dtype, double *out, double *lse) {
+  if (dtype != ORACLE_BF16 && dtype != ORACLE_FP16) return ORACLE_ERR_ARG;
   int rc = check_args(block_table, seqlens, B, s_q, h_q, h_kv, d, dv, page_size, num_pages,
                       max_blocks);
   if (rc != ORACLE_OK) return rc;
@@ -167,9 +201,9 @@ int mla_oracle_decode(const uint16_t *q, const uint16_t *kcache, const int32_t *
       continue;
     }
     row_scores(q + r * d, kcache, block_table, b, g, n_vis, h_kv, d, page_size, max_blocks, scale,
-               s);
+               dtype, s);
     attend_range(s, 0, n_vis, kcache, block_table, b, g, h_kv, d, dv, page_size, max_blocks,
-                 out + r * dv, lse + r);
+                 dtype, out + r * dv, lse + r);
     free(s);
   }
   return failed ? ORACLE_ERR_NOMEM : ORACLE_OK;
@@ -186,8 +220,9 @@ int mla_oracle_decode(const uint16_t *q, const uint16_t *kcache, const int32_t *
 int mla_oracle_decode_split(const uint16_t *q, const uint16_t *kcache, const int32_t *block_table,
                             const int32_t *seqlens, int B, int s_q, int h_q, int h_kv, int d,
                             int dv, int page_size, int num_pages, int max_blocks, int causal,
-                            double scale, const int32_t *cut_ptr, const int32_t *cuts,
+                            double scale, int dtype, const int32_t *cut_ptr, const int32_t *cuts,
                             double *out, double *lse) {
+  if (dtype != ORACLE_BF16 && dtype != ORACLE_FP16) return ORACLE_ERR_ARG;
   int rc = check_args(block_table, seqlens, B, s_q, h_q, h_kv, d, dv, page_size, num_pages,
                       max_blocks);
   if (rc != ORACLE_OK) return rc;
@@ -222,14 +257,14 @@ int mla_oracle_decode_split(const uint16_t *q, const uint16_t *kcache, const int
       continue;
     }
     row_scores(q + r * d, kcache, block_table, b, g, n_vis, h_kv, d, page_size, max_blocks, scale,
-               s);
+               dtype, s);
     for (int k = 0; k < n_pieces; ++k) {
       long j0 = (k == 0) ? 0 : cuts[cut_ptr[b] + k - 1];
       long j1 = (k == n_pieces - 1) ? seqlens[b] : cuts[cut_ptr[b] + k];
       if (j1 > n_vis) j1 = n_vis;
       if (j0 > j1) j0 = j1;
       attend_range(s, j0, j1, kcache, block_table, b, g, h_kv, d, dv, page_size, max_blocks,
-                   o_k + (long)k * dv, lse_k + k);
+                   dtype, o_k + (long)k * dv, lse_k + k);
     }
     /* merge */
     double m = -INFINITY;

@@ -25,8 +25,9 @@ def log(msg: str):
 
 def to_device(w, device="cuda"):
     import torch
-    q = torch.from_numpy(w.q.view(np.int16)).to(device).view(torch.bfloat16)
-    kv = torch.from_numpy(w.kcache.view(np.int16)).to(device).view(torch.bfloat16)
+    t = torch.float16 if w.dtype == "fp16" else torch.bfloat16
+    q = torch.from_numpy(w.q.view(np.int16)).to(device).view(t)
+    kv = torch.from_numpy(w.kcache.view(np.int16)).to(device).view(t)
     bt = torch.from_numpy(np.ascontiguousarray(w.block_table, dtype=np.int32)).to(device)
     sl = torch.from_numpy(np.ascontiguousarray(w.seqlens, dtype=np.int32)).to(device)
     return q, kv, bt, sl
@@ -79,4 +80,4 @@ def subset(w, seqs):
     return Workload(name=w.name + "-subset", q=np.ascontiguousarray(w.q[seqs]), kcache=w.kcache,
                     block_table=np.ascontiguousarray(w.block_table[seqs]),
                     seqlens=np.ascontiguousarray(w.seqlens[seqs]), s_q=w.s_q, h_q=w.h_q,
-                    h_kv=w.h_kv, causal=w.causal, scale=w.scale, meta=dict(w.meta))
+                    h_kv=w.h_kv, causal=w.causal, scale=w.scale, meta=dict(w.meta), dtype=w.dtype)

@@ -63,11 +63,11 @@ FAKE = 1 << 20  # a 16-byte aligned non-null address; never dereferenced: every 
 def decode_call(**over):
     lib = mla._load()
     args = dict(q=FAKE, k=FAKE, bt=FAKE, sl=FAKE, batch=2, s_q=1, h_q=16, h_kv=1, d=576, dv=512,
-                num_pages=8, page=64, max_blocks=4, meta=FAKE, num_parts=8, splits=FAKE, causal=0,
+                dtype=0, num_pages=8, page=64, max_blocks=4, meta=FAKE, num_parts=8, splits=FAKE, causal=0,
                 scale=0.0416, out=FAKE, lse=FAKE, ws=FAKE, ws_bytes=1 << 30, stream=None)
     args.update(over)
     rc = lib.mla_decode(args["q"], args["k"], args["bt"], args["sl"], args["batch"], args["s_q"],
-                        args["h_q"], args["h_kv"], args["d"], args["dv"], args["num_pages"],
+                        args["h_q"], args["h_kv"], args["d"], args["dv"], args["dtype"], args["num_pages"],
                         args["page"], args["max_blocks"], args["meta"], args["num_parts"],
                         args["splits"], args["causal"], args["scale"], args["out"], args["lse"],
                         args["ws"], args["ws_bytes"], args["stream"])
@@ -78,6 +78,8 @@ def decode_call(**over):
     (dict(d=575), "MLA_ERR_UNSUPPORTED"),
     (dict(dv=256), "MLA_ERR_UNSUPPORTED"),
     (dict(page=32), "MLA_ERR_UNSUPPORTED"),
+    (dict(dtype=2), "MLA_ERR_UNSUPPORTED"),
+    (dict(dtype=-1), "MLA_ERR_UNSUPPORTED"),
     (dict(batch=0), "MLA_ERR_INVALID_ARG"),
     (dict(h_q=16, h_kv=3), "MLA_ERR_INVALID_ARG"),
     (dict(s_q=64, h_q=128), "MLA_ERR_UNSUPPORTED"),

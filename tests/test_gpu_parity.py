@@ -22,7 +22,8 @@ def gpu_ready():
 
 
 def ref(w):
-    return oracle.decode(w.q, w.kcache, w.block_table, w.seqlens, causal=w.causal, scale=w.scale)
+    return oracle.decode(w.q, w.kcache, w.block_table, w.seqlens, causal=w.causal, scale=w.scale,
+                         dtype=w.dtype)
 
 
 def case(w, what):
@@ -211,3 +212,29 @@ def test_ceiling_helpers_run():
     mla.mla_ceiling_mfma(fsink, 8, 10)
     torch.cuda.synchronize()
     assert int(isink.item()) == 0 and float(fsink.item()) == 0.0
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_fp16_random_small_shapes(seed):
+    """fp16 q and cache (one page lists FP16 beside BF16) against the oracle
+    reading the same bits as fp16."""
+    rng = np.random.default_rng(700 + seed)
+    B = int(rng.integers(1, 5))
+    s_q = int(rng.integers(1, 4))
+    h_q = int(rng.choice([16, 32, 64, 128]))
+    causal = bool(rng.integers(0, 2))
+    lens = rng.integers(1, 1500, size=B)
+    w = synth.make_workload(lens, s_q=s_q, h_q=h_q, causal=causal, seed=seed, dtype="fp16")
+    case(w, f"fp16 seed {seed}")
+    out, lse = run_gpu(w)
+    check_parity(out, lse, *ref(w), what=f"fp16 seed {seed}")
+
+
+@pytest.mark.parametrize("name,seqs", [("membound", [0, 31]), ("mtp", [5, 63]), ("hkv2", [7])])
+def test_fp16_full_size_sampled(name, seqs):
+    w = synth.named_workload(name, dtype="fp16")
+    case(w, f"full {name} fp16")
+    out, lse = run_gpu(w)
+    sub = subset(w, seqs)
+    rout, rlse = ref(sub)
+    check_parity(out[seqs], lse[seqs], rout, rlse, what=f"{name} fp16 seqs {seqs}")

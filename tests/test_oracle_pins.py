@@ -30,12 +30,19 @@ pytestmark = pytest.mark.filterwarnings("ignore::RuntimeWarning")
 
 def run_oracle(w, **kw):
     return oracle.decode(w.q, w.kcache, w.block_table, w.seqlens, causal=w.causal, scale=w.scale,
-                         **kw)
+                         dtype=w.dtype, **kw)
+
+
+def to64(bits, dtype):
+    """16-bit bit patterns -> float64 by numpy's own conversions."""
+    if dtype == "fp16":
+        return np.ascontiguousarray(bits, dtype=np.uint16).view(np.float16).astype(np.float64)
+    return bf16_to_f32(bits).astype(np.float64)
 
 
 def dense_keys(w, b):
     """[N_b, h_kv, 576] float64 keys of sequence b, gathered with numpy fancy indexing."""
-    kc = bf16_to_f32(w.kcache).astype(np.float64)
+    kc = to64(w.kcache, w.dtype)
     n = int(w.seqlens[b])
     j = np.arange(n)
     return kc[w.block_table[b, j // PAGE], j % PAGE]
@@ -47,7 +54,7 @@ def visible(n, s_q, t, causal):
 
 def dense_reference(w):
     """Brute force: unpaged K/V, full score matrix, masked logsumexp."""
-    q = bf16_to_f32(w.q).astype(np.float64)
+    q = to64(w.q, w.dtype)
     B, s_q, h_q, _ = q.shape
     hpg = h_q // w.h_kv
     out = np.zeros((B, s_q, h_q, DV))
@@ -71,7 +78,7 @@ def dense_reference(w):
     return out, lse
 
 
-def random_tiny(seed):
+def random_tiny(seed, dtype="bf16"):
     rng = np.random.default_rng(10_000 + seed)
     B = int(rng.integers(1, 4))
     s_q = int(rng.integers(1, 5))
@@ -82,7 +89,7 @@ def random_tiny(seed):
     if seed % 5 == 0:
         lens[0] = int(rng.integers(0, 4))          # empty / causal-empty rows
     return synth.make_workload(lens, s_q=s_q, h_q=h_q, h_kv=h_kv, causal=causal, seed=seed,
-                               extra_pages=int(rng.integers(0, 3)))
+                               extra_pages=int(rng.integers(0, 3)), dtype=dtype)
 
 
 def assert_close(a, b, rtol=1e-11, atol=1e-12):
@@ -408,3 +415,49 @@ def test_schedule_rejects_bad_arguments():
         oracle.schedule([1, 2], num_parts=4, fixed_cost=0)
     with pytest.raises(ValueError):
         oracle.schedule([1, -2], num_parts=4, fixed_cost=1)
+
+
+# --------------------------------------------------------------------------
+# fp16 inputs (the element type one page lists beside bf16)
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+def test_widening_matches_numpy_for_every_bit_pattern(dtype):
+    """The oracle's widening of all 65536 patterns equals numpy's (fp16) or the
+    bf16-is-the-top-half-of-binary32 rule evaluated by numpy (bf16)."""
+    bits = np.arange(1 << 16, dtype=np.uint16)
+    got = oracle.widen(bits, dtype)
+    ref = to64(bits, dtype)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_fp16_oracle_matches_dense_brute_force(seed):
+    w = random_tiny(seed, dtype="fp16")
+    out, lse = run_oracle(w)
+    rout, rlse = dense_reference(w)
+    assert_close(lse, rlse, rtol=1e-11, atol=1e-11)
+    assert_close(out, rout, rtol=1e-9, atol=1e-11)
+
+
+def test_fp16_and_bf16_read_the_same_bits_differently():
+    """The same bit patterns give different results per dtype (the dtype is
+    really passed through), and fp16 inputs of bf16-representable values
+    give the bf16 result."""
+    w = random_tiny(3, dtype="fp16")
+    o16, l16 = run_oracle(w)
+    o_b, l_b = oracle.decode(w.q, w.kcache, w.block_table, w.seqlens, causal=w.causal,
+                             scale=w.scale, dtype="bf16")
+    assert not np.allclose(np.nan_to_num(l16), np.nan_to_num(l_b))
+    # values exact in both formats: small integers / 4
+    rng = np.random.default_rng(7)
+    vals = rng.integers(-8, 9, size=w.kcache.shape).astype(np.float32) / 4
+    qv = rng.integers(-8, 9, size=w.q.shape).astype(np.float32) / 4
+    o1, l1 = oracle.decode(qv.astype(np.float16).view(np.uint16), vals.astype(np.float16).view(np.uint16),
+                           w.block_table, w.seqlens, causal=w.causal, scale=w.scale, dtype="fp16")
+    o2, l2 = oracle.decode(bf16_bits(qv), bf16_bits(vals), w.block_table, w.seqlens,
+                           causal=w.causal, scale=w.scale, dtype="bf16")
+    assert_close(o1, o2, rtol=0, atol=0)
+    assert_close(l1, l2, rtol=0, atol=0)
