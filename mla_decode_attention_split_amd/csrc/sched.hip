@@ -170,9 +170,11 @@ __global__ __launch_bounds__(NT) void sched_kernel(const int32_t* __restrict__ s
 }
 
 // Fast variant for up to 1024 sequences and 4096 parts: 256 threads, every
-// per-sequence quantity in LDS, and the first and last sequence of each part
-// found by scattering each sequence's part range (no search, no division per
-// part).  Same output as sched_kernel.
+// per-sequence quantity in LDS.  Each part finds its first and last sequence
+// by binary search over the sequences' last and first parts (both
+// non-decreasing), and the part of a cost position is a multiply by a
+// precomputed reciprocal of T with an exact correction.  Same output as
+// sched_kernel.
 constexpr int kSmallThreads = 256;
 constexpr int kSmallBatch = 1024;
 constexpr int kSmallParts = 4096;
@@ -182,17 +184,12 @@ __global__ __launch_bounds__(kSmallThreads) void sched_small_kernel(
     int32_t* __restrict__ meta, int32_t* __restrict__ num_splits) {
   __shared__ long long C[kSmallBatch + 1];
   __shared__ int SL[kSmallBatch], FP[kSmallBatch], LP[kSmallBatch], NS[kSmallBatch];
-  __shared__ int BB[kSmallParts], BE[kSmallParts];
   __shared__ long long scratch[kSmallThreads / 64];
   const int tid = threadIdx.x;
   const int per = (batch + kSmallThreads - 1) / kSmallThreads;
   const int b0 = tid * per;
   const long long fc = fixed_cost;
 
-  for (int p = tid; p < num_parts; p += kSmallThreads) {
-    BB[p] = batch;  // no sequence: the part stays empty
-    BE[p] = -1;
-  }
   long long local = 0;
   for (int i = 0; i < per; ++i) {
     const int b = b0 + i;
@@ -204,12 +201,24 @@ __global__ __launch_bounds__(kSmallThreads) void sched_small_kernel(
   }
   long long total;
   long long base = block_exclusive_scan<kSmallThreads>(local, scratch, &total);
-  long long T = (total + num_parts - 1) / num_parts;
-  if (T < 1) T = 1;
-  // part of cost position x (32-bit division whenever the positions fit)
+  // positions fit in 31 bits for any realistic batch; 64-bit otherwise
   const bool narrow = total < 0x7fffffffLL;
+  long long T = narrow ? (long long)(((unsigned)total + (unsigned)num_parts - 1u) / (unsigned)num_parts)
+                       : (total + num_parts - 1) / num_parts;
+  if (T < 1) T = 1;
+  // floor(x / T): q = high half of x * floor((2^32 - 1) / T) is at most 2
+  // below the quotient for x < 2^31; the remainder loop corrects it exactly.
+  const unsigned T32 = (unsigned)T;
+  const unsigned rcp = narrow ? 0xffffffffu / T32 : 0u;
   auto part_of = [&](long long x) -> int {
-    return narrow ? (int)((unsigned)x / (unsigned)T) : (int)(x / T);
+    if (!narrow) return (int)(x / T);
+    unsigned q = __umulhi((unsigned)x, rcp);
+    unsigned r = (unsigned)x - q * T32;
+    while (r >= T32) {
+      ++q;
+      r -= T32;
+    }
+    return (int)q;
   };
   long long pieces = 0;
   for (int i = 0; i < per; ++i) {
@@ -239,21 +248,25 @@ __global__ __launch_bounds__(kSmallThreads) void sched_small_kernel(
   if (tid == 0) num_splits[batch] = (int32_t)ptotal;
   __syncthreads();  // FP, LP, C, NS complete
 
-  // Part p's first sequence is the b with LP[b-1] < p <= LP[b]; its last
-  // sequence is the b with FP[b] <= p < FP[b+1].
-  for (int i = 0; i < per; ++i) {
-    const int b = b0 + i;
-    if (b < batch) {
-      const int plo = b == 0 ? 0 : LP[b - 1] + 1;
-      for (int p = plo; p <= LP[b] && p < num_parts; ++p) BB[p] = b;
-      const int phi = b + 1 < batch ? FP[b + 1] : num_parts;
-      for (int p = FP[b]; p < phi && p < num_parts; ++p) BE[p] = b;
-    }
-  }
-  __syncthreads();
-
   for (int p = tid; p < num_parts; p += kSmallThreads) {
-    const int bb = BB[p], be = BE[p];
+    // Part p's first sequence is the smallest b with LP[b] >= p (batch if
+    // none: the part is empty); its last is the largest b with FP[b] <= p
+    // (-1 if none).  Both arrays are non-decreasing in b.
+    int lo = 0, hi = batch;
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (LP[mid] >= p) hi = mid;
+      else lo = mid + 1;
+    }
+    const int bb = lo;
+    lo = 0;
+    hi = batch;
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (FP[mid] > p) hi = mid;
+      else lo = mid + 1;
+    }
+    const int be = lo - 1;
     i32x4 w0 = {0, 0, -1, 0}, w1 = {0, 0, 0, 0};
     if (bb < batch && be >= 0 && bb <= be) {
       const long long lo_key = (long long)p * T, hi_key = (long long)(p + 1) * T;
