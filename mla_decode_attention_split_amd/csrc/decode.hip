@@ -11,11 +11,12 @@
 // partial outputs).
 //
 // Design (gfx950):
-//   * 4 waves per workgroup, one workgroup per CU.  The part's stages (query
-//     rows, then 32-key blocks, per piece) stream through a ring of 4 LDS
+//   * One workgroup per CU: 4 waves for tiles of up to 64 query rows, 8 waves
+//     (two per SIMD) for 128-row tiles.  The part's stages (query rows, then
+//     32-key blocks, per piece) stream through a ring of 4 (8 waves: 3) LDS
 //     slots of 36 KB with 16-byte buffer loads straight into LDS.  Every ring
-//     position is loaded with the same number of instructions; lanes with
-//     nothing to load address past their buffer's range, which costs no
+//     position is loaded with the same number of instructions per wave; lanes
+//     with nothing to load address past their buffer's range, which costs no
 //     memory traffic, so the per-stage waits are exact constants.
 //   * The prologue needs one memory trip after the part's metadata record:
 //     the record carries the lengths and partial slots of the part's first
@@ -31,10 +32,13 @@
 //     share of the 576 dims (and, with DG = 4, one of the two 16-key blocks),
 //     then exchange fp32 partial scores through LDS and add them in a fixed
 //     order, so every wave of the group holds bit-identical scores.
-//   * Software pipeline: in the iteration of key block s a wave computes the
-//     partial scores of block s while it finishes block s - 1 (partial-score
-//     sum, softmax, P V); the MFMAs of one overlap the vector work of the
-//     other, and one barrier per stage serves both the ring and the exchange.
+//   * Software pipeline (4-wave tiles): in the iteration of key block s a
+//     wave computes the partial scores of block s while it finishes block
+//     s - 1 (partial-score sum, softmax, P V); the MFMAs of one overlap the
+//     vector work of the other, and one barrier per stage serves both the ring
+//     and the exchange.  8-wave tiles have no registers for that; they run
+//     each stage in order and rely on the second wave of the SIMD instead,
+//     and keep the Q^T fragments of the rope dims in LDS.
 //   * Softmax in fp32 in the log2 domain; the running max is raised only when
 //     a row's new max exceeds it by more than kTau (then O and l are
 //     rescaled).  P is rounded to bf16 for the MFMA and a second row sum adds
@@ -125,7 +129,10 @@ template <int R, int RG, int DG>
 struct Tile {
   static constexpr int NW = RG * DG;
   static constexpr int BM = R * RG;                      // query rows per workgroup
-  static constexpr int LPW = kLoadsPerStage / NW;        // 16-byte loads per lane per stage
+  // 16-byte loads per lane per stage; with 8 waves the last load is issued
+  // by the first LAST_WAVES waves only (36 = 4 x 8 + 4)
+  static constexpr int LPW = (kLoadsPerStage + NW - 1) / NW;
+  static constexpr int LAST_WAVES = kLoadsPerStage - (LPW - 1) * NW;
   static constexpr int KSTEPS = R == 32 ? 36 : 18;       // score k-steps over 576 dims
   static constexpr int KSPLIT = 2;                       // k-step interleave among DG waves
   static constexpr int KBSPLIT = DG / KSPLIT;            // 16-key blocks split among waves (R = 16)
@@ -137,23 +144,36 @@ struct Tile {
   static constexpr int XCH_ONE = NW * KB_W * PARTIAL_BYTES;    // one exchange buffer
   // 16-row tiles double-buffer the exchange; 32-row tiles have room for one
   // buffer and separate its reads from the next writes with a barrier.
-  static constexpr int XCH_BUFS = R == 32 ? 1 : 2;
+  static constexpr int XCH_BUFS = (R == 32 || NW == 8) ? 1 : 2;
+  // 8-wave 32-row tiles (128 rows, two waves per SIMD) are not software
+  // pipelined: each stage's scores, softmax and P V run in order, and the
+  // other wave of the SIMD fills the gaps.  Their ring has 3 slots (stage s
+  // is computed while s + 1 and s + 2 load), which leaves room for the
+  // 8-wave exchange buffer.
+  static constexpr bool FLAT = NW == 8 && R == 32;
+  static constexpr int SLOTS = FLAT ? 3 : kSlots;
+  static constexpr int RING_BYTES = SLOTS * kStageBytes;
+  // FLAT tiles keep the Q^T fragments of the rope dims (the last QR_STEPS
+  // k-steps of each wave) in LDS instead of registers
+  static constexpr int QR_STEPS = FLAT ? 2 : 0;
+  static constexpr int QREG_STEPS = KS_W - QR_STEPS;     // Q^T k-steps held in registers
+  static constexpr int QR_BYTES = NW * QR_STEPS * 1024;
   static constexpr int NQ = (BM + kStage - 1) / kStage;  // query stages per piece
   static constexpr int QK_MFMA = KS_W * KB_W;
   static constexpr int PV_MFMA = R == 32 ? 2 * NT : NT;
   static constexpr int NSLOT = QK_MFMA + PV_MFMA;        // points where loads are issued
-  static_assert(NW == kWaves, "four waves per workgroup");
+  static_assert(NW == 4 || NW == 8, "four or eight waves per workgroup");
   static_assert(DG >= 2 && DG % 2 == 0, "split-K tiles only");
-  static_assert(LPW * NW == kLoadsPerStage, "stage loads split evenly");
+  static_assert(LAST_WAVES > 0 && LAST_WAVES <= NW, "stage loads split over the waves");
   static_assert(KS_W * KSPLIT == KSTEPS && KBSPLIT * KSPLIT == DG, "score split");
   static_assert(R == 16 || KBSPLIT == 1, "key-block split only for 16-row tiles");
   static_assert(NSLOT >= LPW, "one load per issue point at most");
   static_assert(2 * LPW < 63, "vector memory counter capacity");
-  static_assert(kLdsBytes + XCH_BUFS * XCH_ONE <= 163840, "LDS capacity");
+  static_assert(RING_BYTES + XCH_BUFS * XCH_ONE + QR_BYTES <= 163840, "LDS capacity");
 };
 
 template <int R, int RG, int DG, bool QG, typename E>
-__global__ __launch_bounds__(256, 1) void decode_kernel(
+__global__ __launch_bounds__(64 * RG * DG, 1) void decode_kernel(
     const uint16_t* __restrict__ q_ptr, const uint16_t* __restrict__ kv_ptr,
     const int32_t* __restrict__ block_table, const int32_t* __restrict__ seqlens,
     const int32_t* __restrict__ meta, uint16_t* __restrict__ out, float* __restrict__ lse,
@@ -164,13 +184,15 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(
   using OAcc = typename std::conditional<R == 32, f32x16, f32x4>::type;
   constexpr int SREGS = R == 32 ? 16 : 8;  // scores per lane per stage
 
-  __shared__ __attribute__((aligned(1024))) char lds_raw[kLdsBytes + T::XCH_BUFS * T::XCH_ONE];
+  __shared__ __attribute__((aligned(1024))) char lds_raw[T::RING_BYTES + T::XCH_BUFS * T::XCH_ONE + T::QR_BYTES];
   char MLA_LDS* lds = (char MLA_LDS*)lds_raw;
-  char MLA_LDS* xch0 = lds + kLdsBytes;
+  char MLA_LDS* xch0 = lds + T::RING_BYTES;
 
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int lane = tid & 63;
+  // this wave's Q^T rope fragments (FLAT tiles): step j at qr0 + 1024 j
+  char MLA_LDS* qr0 = xch0 + T::XCH_BUFS * T::XCH_ONE + w * T::QR_STEPS * 1024 + lane * 16;
   const int rg = w / DG;
   const int dg = w % DG;
   const int kh = dg % T::KSPLIT;   // k-step share: steps ks = 2 j + kh
@@ -364,7 +386,10 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(
   // valid row.  Otherwise (QG) every lane's offset is computed.
   bool pend_q = false;
   unsigned qoff[QG ? LPW : 1];
+  // waves past LAST_WAVES skip the stage's last load
+  const bool all_loads = T::LAST_WAVES == NW || w < T::LAST_WAVES;
   auto fire = [&](int k) {
+    if (k == LPW - 1 && !all_loads) return;
     if constexpr (QG) load_lds16(pend, pend_q ? qoff[k] : loff[k], pend_dst + k * NW * 1024);
     else load_lds16(pend, loff[k], pend_dst + k * NW * 1024);
   };
@@ -439,12 +464,16 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(
   fire_all();
 
   int cstage = 0;
-  auto slot_of = [&](int c) { return lds + (c & (kSlots - 1)) * kStageBytes; };
+  auto slot_of = [&](int c) {
+    if constexpr (T::SLOTS == 3) return lds + (c % 3) * kStageBytes;  // c >= 0 here
+    else return lds + (c & (kSlots - 1)) * kStageBytes;
+  };
   // Wait for stream position cstage (position cstage + 1 may stay in flight),
   // then a barrier: the stage and the previous iteration's partial scores are
   // visible to all waves, and the slot refilled next has been read by all.
   auto stage_ready = [&]() {
-    wait_vmcnt<LPW>();
+    if (all_loads) wait_vmcnt<LPW>();
+    else wait_vmcnt<LPW - 1>();
     block_barrier();
   };
   // query rows of this wave inside its query stage
@@ -468,7 +497,7 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) o[nt] = OAcc{};
     float m_run = kMinit, l_run = 0.f, lr_run = 0.f;
-    i16x8 qf[KS_W];
+    i16x8 qf[T::QREG_STEPS];
 
     // Mask the raw scores of key stage sp (keys past the end, or past the
     // row's causal limit).  The scale (positive) is applied later: to the
@@ -683,6 +712,58 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(
       else fire_from(T::QK_MFMA);
     };
 
+    // FLAT tiles: a stage's partial scores, their exchange with the other
+    // wave of the row group (each wave keeps its own partial and adds the
+    // partner's; the two sums are bit-identical since fp32 addition commutes),
+    // softmax and P V.
+    auto flat_scores = [&](const char MLA_LDS* __restrict__ rd) -> f32x16 {
+      f32x16 sacc = f32x16{};
+      if constexpr (T::FLAT) {
+        constexpr int NK = KS_W;
+        constexpr int KP = 2;  // K fragments read ahead (registers are tight at 2 waves per SIMD)
+        i16x8 kf[KP];
+#pragma unroll
+        for (int i = 0; i < KP; ++i) kf[i] = lds_read_b128(rd + kstep_off(i));
+        __builtin_amdgcn_sched_barrier(0);
+        i16x8 qrf[T::QR_STEPS];
+#pragma unroll
+        for (int i = 0; i < NK; ++i) {
+          if (i == T::QREG_STEPS - 4) {  // the rope fragments, a few MFMAs ahead
+#pragma unroll
+            for (int j = 0; j < T::QR_STEPS; ++j) qrf[j] = lds_read_b128(qr0 + 1024 * j);
+          }
+          if (i < T::QREG_STEPS) sacc = E::mfma32(kf[i % KP], qf[i < T::QREG_STEPS ? i : 0], sacc);
+          else sacc = E::mfma32(kf[i % KP], qrf[i >= T::QREG_STEPS ? i - T::QREG_STEPS : 0], sacc);
+          if (i + KP < NK) kf[i % KP] = lds_read_b128(rd + kstep_off(i + KP));
+          fire_slot(i);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int qd = 0; qd < 4; ++qd)
+          lds_write_f4(xch0 + w * 4096 + qd * 1024 + lane * 16,
+                       f32x4{sacc[4 * qd], sacc[4 * qd + 1], sacc[4 * qd + 2], sacc[4 * qd + 3]});
+      }
+      return sacc;
+    };
+    // Full scores of stage sp (own partial + the partner's), softmax and P V
+    // with the keys of ring slot st.
+    auto flat_finish = [&](const f32x16& own, int sp, const char MLA_LDS* __restrict__ st, int first_slot) {
+      if constexpr (T::FLAT) {
+        float x[SREGS];
+        const char MLA_LDS* pp = xch0 + (w ^ 1) * 4096 + lane * 16;
+#pragma unroll
+        for (int qd = 0; qd < 4; ++qd) {
+          const f32x4 u = lds_read_f4(pp + qd * 1024);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) x[4 * qd + e] = own[4 * qd + e] + u[e];
+        }
+        prep(x, sp);
+        SoftState ss;
+#pragma unroll
+        for (int j = 0; j < kSoftSlices; ++j) soft_slice(x, ss, j);
+        pv(ss.pw, ss.rescale, ss.alpha, sp, st, first_slot);
+      }
+    };
     if (nst > 0) {
       for (int jq = 0; jq < NQ; ++jq, ++cstage) {
         stage_ready();
@@ -692,12 +773,25 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(
           if (jq == q_stage) {
             const char MLA_LDS* qs = rd + q_row0 * kRowBytes;
 #pragma unroll
-            for (int ks = 0; ks < KS_W; ++ks) qf[ks] = lds_read_b128(qs + kstep_off(ks));
+            for (int ks = 0; ks < T::QREG_STEPS; ++ks) qf[ks] = lds_read_b128(qs + kstep_off(ks));
+#pragma unroll
+            for (int j = 0; j < T::QR_STEPS; ++j)
+              lds_write_f4(qr0 + 1024 * j,
+                           __builtin_bit_cast(f32x4, lds_read_b128(qs + kstep_off(T::QREG_STEPS + j))));
           }
         }(slot_of(cstage), slot_of(cstage + 2));
       }
       using F = std::false_type;
       using Tr = std::true_type;
+      if constexpr (T::FLAT) {
+        for (int s = 0; s < nst; ++s, ++cstage) {
+          stage_ready();
+          plan(slot_of(cstage + 2));
+          const f32x16 sc = flat_scores(slot_of(cstage));
+          block_barrier();  // the partial scores are exchanged
+          flat_finish(sc, s, slot_of(cstage), T::QK_MFMA);
+        }
+      } else {
       // stage 0: scores only
       stage_ready();
       plan(slot_of(cstage + 2));
@@ -714,6 +808,7 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(
       block_barrier();
       const char MLA_LDS* xr = xch0 + (T::XCH_BUFS == 2 ? ((nst - 1) & 1) * T::XCH_ONE : 0);
       kv_step(Tr{}, F{}, slot_of(cstage), slot_of(cstage - 1), nullptr, xr, nst);
+      }
     }
 
     // ---- epilogue: normalise and write this piece --------------------------
@@ -779,16 +874,18 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(
   template __global__ void decode_kernel<16, 1, 4, false, E>(MLA_DECODE_PARAMS);   \
   template __global__ void decode_kernel<16, 2, 2, false, E>(MLA_DECODE_PARAMS);   \
   template __global__ void decode_kernel<32, 2, 2, false, E>(MLA_DECODE_PARAMS);   \
+  template __global__ void decode_kernel<32, 4, 2, false, E>(MLA_DECODE_PARAMS);   \
   template __global__ void decode_kernel<16, 1, 4, true, E>(MLA_DECODE_PARAMS);    \
   template __global__ void decode_kernel<16, 2, 2, true, E>(MLA_DECODE_PARAMS);    \
-  template __global__ void decode_kernel<32, 2, 2, true, E>(MLA_DECODE_PARAMS);
+  template __global__ void decode_kernel<32, 2, 2, true, E>(MLA_DECODE_PARAMS);    \
+  template __global__ void decode_kernel<32, 4, 2, true, E>(MLA_DECODE_PARAMS);
 MLA_DECODE_INSTANCES(Bf16)
 MLA_DECODE_INSTANCES(F16)
 
 template <int R, int RG, int DG, bool QG, typename E>
 static hipError_t launch_t(const DecodeArgs& a, hipStream_t stream) {
   const int grid = a.num_parts * a.m_tiles * a.h_kv;
-  hipLaunchKernelGGL((decode_kernel<R, RG, DG, QG, E>), dim3(grid), dim3(256), 0, stream, a.q, a.kv,
+  hipLaunchKernelGGL((decode_kernel<R, RG, DG, QG, E>), dim3(grid), dim3(64 * RG * DG), 0, stream, a.q, a.kv,
                      a.block_table, a.seqlens, a.meta, a.out, a.lse, a.o_part, a.lse_part, a);
   return hipGetLastError();
 }
@@ -799,6 +896,7 @@ static hipError_t launch_q(const DecodeArgs& a, int tile_rows, hipStream_t strea
     case 16: return launch_t<16, 1, 4, QG, E>(a, stream);
     case 32: return launch_t<16, 2, 2, QG, E>(a, stream);
     case 64: return launch_t<32, 2, 2, QG, E>(a, stream);
+    case 128: return launch_t<32, 4, 2, QG, E>(a, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -21,7 +21,6 @@ constexpr int kStageBytes = kStage * kRowBytes;    // 36864 B
 constexpr int kSlots = 4;                          // LDS ring of stages
 constexpr int kLdsBytes = kSlots * kStageBytes;    // 147456 B of 160 KB
 constexpr int kLoadsPerStage = kStageBytes / 1024; // 1 KB per wave-wide 16 B load
-constexpr int kWaves = 4;
 constexpr int kMetaWords = 8;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));

@@ -39,7 +39,7 @@ struct CombineArgs {
 
 // Query rows per workgroup for M rows per KV head (16, 32 or 64; larger M
 // takes several 64-row tiles).
-inline int tile_rows_for(int M) { return M <= 16 ? 16 : M <= 32 ? 32 : 64; }
+inline int tile_rows_for(int M) { return M <= 16 ? 16 : M <= 32 ? 32 : M <= 64 ? 64 : 128; }
 
 hipError_t launch_sched(const int32_t* seqlens, int batch, int num_parts, int fixed_cost,
                         int32_t* meta, int32_t* num_splits, hipStream_t stream);

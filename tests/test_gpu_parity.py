@@ -171,6 +171,17 @@ def test_two_kv_heads():
     check_parity(out, lse, *ref(w), what="h_kv=2")
 
 
+@pytest.mark.parametrize("h_q,s_q,h_kv", [(128, 2, 2), (64, 3, 2), (128, 4, 4)])
+def test_kv_heads_many_rows(h_q, s_q, h_kv):
+    """Several KV heads with more than 64 query rows per head (the 128-row,
+    8-wave tile with per-lane query offsets), including a partial row tile."""
+    w = synth.make_workload([700, 129, 64], s_q=s_q, h_q=h_q, h_kv=h_kv, causal=True,
+                            seed=27 + h_q + s_q)
+    case(w, f"h_kv={h_kv} rows {w.rows_per_kv_head}")
+    out, lse = run_gpu(w)
+    check_parity(out, lse, *ref(w), what=f"h_kv={h_kv} M={w.rows_per_kv_head}")
+
+
 def test_constant_value_rows():
     w = synth.make_workload([500, 37], s_q=1, h_q=16, seed=26)
     c = synth.bf16_bits(np.array([-1.375], dtype=np.float32))[0]
