@@ -71,6 +71,50 @@ def test_edge_lengths(s_q, causal):
     check_parity(out, lse, *ref(w), what=f"edge s_q={s_q}")
 
 
+@pytest.mark.parametrize("case_name", ["all_empty", "one", "ones", "leading_empty", "trailing_empty",
+                                       "more_parts_than_units", "one_long_many_short"])
+def test_metadata_bitexact_edges(case_name):
+    """Batches that put part boundaries on empty sequences, leave parts with no
+    sequence, or pack many sequences into one part (the per-part search for the
+    first and last sequence at its limits)."""
+    import mla_decode_attention_split_amd as mla
+    import torch
+    lens = {
+        "all_empty": np.zeros(40, np.int32),
+        "one": np.array([5000], np.int32),
+        "ones": np.ones(300, np.int32),
+        "leading_empty": np.concatenate([np.zeros(100, np.int32), np.full(20, 3000, np.int32)]),
+        "trailing_empty": np.concatenate([np.full(20, 3000, np.int32), np.zeros(100, np.int32)]),
+        "more_parts_than_units": np.array([31, 0, 33, 1], np.int32),
+        "one_long_many_short": np.concatenate([np.array([65536], np.int32),
+                                               np.full(500, 7, np.int32)]),
+    }[case_name]
+    for num_parts, fixed_cost in [(1, 1), (8, 2), (256, 2), (4096, 3)]:
+        log(f"[case] metadata edge {case_name}: B={lens.size} parts={num_parts} fixed={fixed_cost}")
+        sl = torch.from_numpy(lens).cuda()
+        meta, splits = mla.mla_get_metadata(sl, 16, 1, num_parts=num_parts, fixed_cost=fixed_cost)
+        torch.cuda.synchronize()
+        rmeta, rsplits = oracle.schedule(lens, num_parts=num_parts, fixed_cost=fixed_cost,
+                                         unit_tokens=32)
+        np.testing.assert_array_equal(meta.cpu().numpy(), rmeta)
+        np.testing.assert_array_equal(splits.cpu().numpy(), rsplits)
+
+
+def test_metadata_shape_tiles():
+    """Tile rows, fixed cost and default part count follow the row count: 64-row
+    tiles up to 64 rows per KV head, 128-row tiles (8 waves) above."""
+    import mla_decode_attention_split_amd as mla
+    import torch
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    for M, h_kv, tr in [(16, 1, 16), (32, 1, 32), (64, 1, 64), (65, 1, 128), (256, 1, 128),
+                        (128, 2, 128)]:
+        parts, fixed, tile = mla.mla_get_metadata_shape(32, M, h_kv)
+        assert tile == tr, (M, tile)
+        assert fixed == (tr + 31) // 32 + 1
+        per = cus // (((M + tr - 1) // tr) * h_kv)
+        assert parts == (per // 8 * 8 if per >= 8 else 8), (M, h_kv, parts)
+
+
 def test_metadata_bitexact():
     import mla_decode_attention_split_amd as mla
     rng = np.random.default_rng(7)
