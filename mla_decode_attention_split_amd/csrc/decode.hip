@@ -192,7 +192,7 @@ __global__ __launch_bounds__(64 * RG * DG, 1) void decode_kernel(
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int lane = tid & 63;
   // this wave's Q^T rope fragments (FLAT tiles): step j at qr0 + 1024 j
-  char MLA_LDS* qr0 = xch0 + T::XCH_BUFS * T::XCH_ONE + w * T::QR_STEPS * 1024 + lane * 16;
+  char MLA_LDS* qr0 = T::FLAT ? xch0 + T::XCH_BUFS * T::XCH_ONE + w * T::QR_STEPS * 1024 + lane * 16 : lds;
   const int rg = w / DG;
   const int dg = w % DG;
   const int kh = dg % T::KSPLIT;   // k-step share: steps ks = 2 j + kh
@@ -764,6 +764,7 @@ __global__ __launch_bounds__(64 * RG * DG, 1) void decode_kernel(
         pv(ss.pw, ss.rescale, ss.alpha, sp, st, first_slot);
       }
     };
+
     if (nst > 0) {
       for (int jq = 0; jq < NQ; ++jq, ++cstage) {
         stage_ready();
