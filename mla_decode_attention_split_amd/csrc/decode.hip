@@ -480,6 +480,56 @@ __global__ __launch_bounds__(64 * RG * DG, 1) void decode_kernel(
   const int q_stage = (rg * R) / kStage;
   const int q_row0 = (rg * R) % kStage;
 
+  // Write the normalised output of one piece (scaled by `scale`): bf16 out and
+  // lse for a whole sequence, else fp32 partials for the combine.
+  auto write_piece = [&](const OAcc* oo, float scale, bool whole_, long long row, float lse_v) {
+    if (my_row >= M) return;
+    const bool lse_writer = dg == 0 && lane < R;
+    // dims held by this lane: 4 consecutive dims per group of 4 accumulators
+    auto dim_of = [&](int nt, int qd) {
+      const int nb = dg * NT + nt;
+      return R == 32 ? 32 * nb + 8 * qd + 4 * (lane >> 5) : 16 * nb + 4 * (lane >> 4);
+    };
+    constexpr int QUADS = OREGS / 4;
+    if (whole_) {
+      if (lse_writer) lse[row] = lse_v;
+      uint16_t* orow = out + row * kValueDim;
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+#pragma unroll
+        for (int qd = 0; qd < QUADS; ++qd) {
+          uint2 pk;
+          pk.x = E::pack(oo[nt][4 * qd + 0] * scale, oo[nt][4 * qd + 1] * scale);
+          pk.y = E::pack(oo[nt][4 * qd + 2] * scale, oo[nt][4 * qd + 3] * scale);
+          *reinterpret_cast<uint2*>(orow + dim_of(nt, qd)) = pk;
+        }
+      }
+    } else {
+      if (lse_writer) lse_part[row] = lse_v;
+      float* prow = o_part + row * kValueDim;
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+#pragma unroll
+        for (int qd = 0; qd < QUADS; ++qd) {
+          *reinterpret_cast<float4*>(prow + dim_of(nt, qd)) =
+              make_float4(oo[nt][4 * qd + 0] * scale, oo[nt][4 * qd + 1] * scale,
+                          oo[nt][4 * qd + 2] * scale, oo[nt][4 * qd + 3] * scale);
+        }
+      }
+    }
+  };
+  // 16-row tiles hold the normalised output of the first piece that is not
+  // the part's last in registers and write it after the last piece: stores
+  // issued between pieces would be waited for by the next stage's vmcnt wait
+  // (the counter covers stores as well as loads).  32-row tiles have too few
+  // spare registers (the 4-wave tile measured slower with it).
+  constexpr bool DEFER = R == 16;
+  OAcc o_def[DEFER ? NT : 1];
+  bool def_pending = false;  // uniform over the workgroup
+  bool def_whole = false;
+  long long def_row = 0;
+  float def_lse = 0.f;
+
   for (int j = 0; j < npieces; ++j) {
     const int b = bb + j;
     const int N = piece_n(j);
@@ -824,43 +874,25 @@ __global__ __launch_bounds__(64 * RG * DG, 1) void decode_kernel(
     const bool empty = !(lt > 0.f);
     const float inv = empty ? 0.f : 1.f / ltr;
     const float lse_row = empty ? -INFINITY : (m_run + fast_log2(lt)) * kLn2;
-    if (my_row < M) {
-      const long long out_row = ((long long)b * a.s_q + q_t) * a.h_q + q_h;
-      const long long part_row = ((long long)slot * a.h_kv + g) * M + my_row;
-      const bool lse_writer = dg == 0 && lane < R;
-      // dims held by this lane: 4 consecutive dims per group of 4 accumulators
-      auto dim_of = [&](int nt, int qd) {
-        const int nb = dg * NT + nt;
-        return R == 32 ? 32 * nb + 8 * qd + 4 * (lane >> 5) : 16 * nb + 4 * (lane >> 4);
-      };
-      constexpr int QUADS = OREGS / 4;
-      if (whole) {
-        if (lse_writer) lse[out_row] = lse_row;
-        uint16_t* orow = out + out_row * kValueDim;
+    const long long row = whole ? ((long long)b * a.s_q + q_t) * a.h_q + q_h
+                                : ((long long)slot * a.h_kv + g) * M + my_row;
+    if constexpr (DEFER) {
+      if (j < npieces - 1 && !def_pending) {
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
+        for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-          for (int qd = 0; qd < QUADS; ++qd) {
-            uint2 pk;
-            pk.x = E::pack((o[nt][4 * qd + 0]) * inv, (o[nt][4 * qd + 1]) * inv);
-            pk.y = E::pack((o[nt][4 * qd + 2]) * inv, (o[nt][4 * qd + 3]) * inv);
-            *reinterpret_cast<uint2*>(orow + dim_of(nt, qd)) = pk;
-          }
-        }
-      } else {
-        if (lse_writer) lse_part[part_row] = lse_row;
-        float* prow = o_part + part_row * kValueDim;
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-#pragma unroll
-          for (int qd = 0; qd < QUADS; ++qd) {
-            *reinterpret_cast<float4*>(prow + dim_of(nt, qd)) =
-                make_float4((o[nt][4 * qd + 0]) * inv, (o[nt][4 * qd + 1]) * inv,
-                            (o[nt][4 * qd + 2]) * inv, (o[nt][4 * qd + 3]) * inv);
-          }
-        }
+          for (int i = 0; i < OREGS; ++i) o_def[nt][i] = o[nt][i] * inv;
+        def_pending = true;
+        def_whole = whole;
+        def_row = row;
+        def_lse = lse_row;
+        continue;
       }
     }
+    write_piece(o, inv, whole, row, lse_row);
+  }
+  if constexpr (DEFER) {
+    if (def_pending) write_piece(o_def, 1.f, def_whole, def_row, def_lse);
   }
   // Out-of-range loads past the end of the stream may still be in flight:
   // they must land before the workgroup's LDS is released.
