@@ -4,9 +4,9 @@
 //
 //   * stream_ceiling_kernel: every workgroup streams a list of cache pages
 //     (64 rows x 1152 B, one KV head) through a 4-slot LDS ring of
-//     36,864-byte stages with 16-byte LDS-DMA loads, two stages ahead of the
-//     stage being read: the memory side of the main kernel's memory-bound
-//     tile, with no arithmetic.  Its rate is the practical HBM read ceiling
+//     36,864-byte stages with 16-byte non-temporal LDS-DMA loads, two stages
+//     ahead of the stage being read: the memory side of the main kernel's
+//     memory-bound tile, with no arithmetic.  Its rate is the practical HBM read ceiling
 //     for that access pattern.
 //   * mfma_ceiling_kernel: every wave runs four independent chains of
 //     32x32x16 bf16 MFMAs: the dense bf16 MFMA rate at the clock the chip
@@ -17,6 +17,7 @@
 namespace mla {
 
 constexpr int kCeilWaves = 4;
+constexpr int kCeilCpolNT = 2;  // non-temporal loads, as the main kernel uses for unshared pages
 constexpr int kCeilLoadsPerWave = kLoadsPerStage / kCeilWaves;  // 9 x 16 B x 64 lanes per stage
 
 __global__ __launch_bounds__(64 * kCeilWaves, 1) void stream_ceiling_kernel(
@@ -39,7 +40,7 @@ __global__ __launch_bounds__(64 * kCeilWaves, 1) void stream_ceiling_kernel(
     for (int k = 0; k < kCeilLoadsPerWave; ++k) {
       const int chunk = k * kCeilWaves + w;
       const unsigned off = page < pool_bytes / (2u * kStageBytes) ? base + chunk * 1024 + lane * 16 : 0x80000000u;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (void MLA_LDS*)(dst + chunk * 1024), 16, off, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (void MLA_LDS*)(dst + chunk * 1024), 16, off, 0, 0, kCeilCpolNT);
     }
   };
   unsigned acc = 0;
