@@ -129,7 +129,7 @@ __device__ __forceinline__ i16x8 cat(i16x4 a, i16x4 b) {
 }
 
 // Tile shape.  R rows per wave (32x32x16 MFMA for R = 32, 16x16x32 for
-// R = 16), RG row groups x DG value-dim groups = 4 waves.
+// R = 16), RG row groups x DG value-dim groups = 4 or 8 waves.
 template <int R, int RG, int DG>
 struct Tile {
   static constexpr int NW = RG * DG;
@@ -353,8 +353,9 @@ __global__ __launch_bounds__(64 * RG * DG, 1) void decode_kernel(
   // ---- stage stream -----------------------------------------------------------
   // For every non-empty piece: NQ query stages (32 rows of the tile each, same
   // swizzled row layout as the keys), then the piece's key stages.  Stream
-  // position c uses ring slot c % 4; position c + 2 is loaded while position c
-  // is computed.  Past the end of the stream the loads are out of range.
+  // position c uses ring slot c % SLOTS; position c + 2 is loaded while
+  // position c is computed.  Past the end of the stream the loads are out of
+  // range.
   // Cursor of the stream: piece lj, query stage lq, key token ltok (end lhi),
   // and the next key stage's page-list position lpos and page half lhalf.
   int lj = 0, lq = 0, ltok = tb, lhi = (bb == be) ? te : n_first;
