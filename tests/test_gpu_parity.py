@@ -151,6 +151,21 @@ def test_split_count_does_not_change_result(num_parts):
     check_parity(out, lse, *ref(w), what=f"parts={num_parts}")
 
 
+@pytest.mark.parametrize("h_q,s_q", [(16, 1), (32, 1), (64, 1), (16, 8)])
+@pytest.mark.parametrize("num_parts", [3, 8])
+def test_many_pieces_per_part(h_q, s_q, num_parts):
+    """Parts that hold many short sequences, some empty, for every tile shape:
+    the piece epilogues (the first non-last piece's output held back to the
+    end of the part in 16-row tiles, the others written at once)."""
+    rng = np.random.default_rng(60 + h_q + s_q + num_parts)
+    lens = rng.integers(1, 400, size=30)
+    lens[[3, 11, 12, 25]] = 0
+    w = synth.make_workload(lens, s_q=s_q, h_q=h_q, causal=s_q > 1, seed=61 + num_parts)
+    case(w, f"many pieces per part, parts={num_parts}")
+    out, lse = run_gpu(w, num_parts=num_parts)
+    check_parity(out, lse, *ref(w), what=f"h_q={h_q} s_q={s_q} parts={num_parts}")
+
+
 @pytest.mark.parametrize("lens,num_parts,h_q,s_q", [([10000], 17, 16, 1), ([10000], 100, 16, 1),
                                                      ([20000, 50], 129, 32, 2), ([3000, 9000, 1], 160, 16, 3)])
 def test_combine_many_pieces(lens, num_parts, h_q, s_q):
