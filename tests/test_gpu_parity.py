@@ -241,6 +241,36 @@ def test_kv_heads_many_rows(h_q, s_q, h_kv):
     check_parity(out, lse, *ref(w), what=f"h_kv={h_kv} M={w.rows_per_kv_head}")
 
 
+def test_pool_past_4gib():
+    """Pages at the top of a cache pool larger than 4 GiB (64-bit byte offsets
+    of pages): the used pages of a small workload are placed at the pool's
+    end, the block table shifted to match; the oracle runs on the compact pool."""
+    import torch
+    w = synth.make_workload([5000, 3000, 77], s_q=2, h_q=32, causal=True, seed=71)
+    q, kv, bt, sl = to_device(w)
+    num_pages = 60000  # 60000 x 73,728 B = 4.42 GB
+    used = kv.shape[0]
+    base = num_pages - used
+    assert base * 64 * 1152 > (1 << 32)
+    log(f"[case] pool of {num_pages} pages, used pages from index {base}")
+    big = torch.zeros((num_pages,) + tuple(kv.shape[1:]), dtype=kv.dtype, device=kv.device)
+    big[base:] = kv
+    out, lse = run_gpu(w, tensors=(q, big, bt + base, sl))
+    del big
+    torch.cuda.empty_cache()
+    check_parity(out, lse, *ref(w), what="pool past 4 GiB")
+
+
+@pytest.mark.parametrize("lens,s_q,h_q", [([131072], 1, 16), ([65536, 1000], 2, 64)])
+def test_long_sequences(lens, s_q, h_q):
+    """Sequences of 64K and 128K keys, split over every part of the default
+    partition (hundreds of pieces per sequence) and merged by the combine."""
+    w = synth.make_workload(lens, s_q=s_q, h_q=h_q, causal=s_q > 1, seed=72 + s_q)
+    case(w, f"long sequences {lens}")
+    out, lse = run_gpu(w)
+    check_parity(out, lse, *ref(w), what=f"long {lens}")
+
+
 def test_constant_value_rows():
     w = synth.make_workload([500, 37], s_q=1, h_q=16, seed=26)
     c = synth.bf16_bits(np.array([-1.375], dtype=np.float32))[0]
