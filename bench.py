@@ -5,11 +5,17 @@ One step = the whole path over one batch of synthetic input: the split-KV
 metadata call (mla_get_metadata), the main kernel (mla_decode_splitkv) and
 the split combine (mla_decode_combine), all on the current stream.
 
-Default workload ("membound"): B=32, s_q=1, h_q=16, h_kv=1, every N=4096,
-page 64, bf16 N(0,1) data, scale 576^-0.5.  Inputs are resident in HBM before
+The metric has two halves, and the default run measures both:
+  * "membound" (the memory-bound half, HBM TB/s at h_q=16): B=32, s_q=1,
+    h_q=16, h_kv=1, every N=4096; its figures are the line's top-level
+    value / roofline;
+  * "mtp" (the compute-bound half, TFLOPS at h_q=128): B=64, s_q=2 causal,
+    h_q=128, N ~ U{1024..8192}; its figures are under "compute_bound", with a
+    roofline against the bf16 MFMA peak.
+Page 64, bf16 N(0,1) data, scale 576^-0.5.  Inputs are resident in HBM before
 the timed region; every step reads a different copy of the KV pool (copies
 rotate over >= 1 GiB) so that the 256 MB Infinity Cache cannot serve the
-pool from the previous step.
+pool from the previous step.  --workload W measures only W.
 
 Output: one JSON line on stdout (details on stderr).
   value       algorithmic bytes per step / time per step (TB/s); bytes =
@@ -21,15 +27,18 @@ Output: one JSON line on stdout (details on stderr).
               2.5 PFLOP/s bf16 for MFMA-bound workloads); traffic = HBM bytes
               per launch from the committed rocprofv3 counter summary when it
               matches the current kernel source, else null
-  cpu_baseline  the CPU oracle (fp64, OpenMP) on the same workload
+  gpu_torch_baseline  plain PyTorch on the GPU, same inputs (context)
+  cpu_baseline  the CPU oracle (fp64, OpenMP) on the primary workload
+  oracle_parity  the timed step's whole output against the oracle
 
 Profile summaries: `--summarize-profiles DIR` turns the rocprofv3 output that
 the commands below leave in DIR into the text summaries and the counter file
-under profiles/ (run from /tmp, TMPDIR=/tmp; WL = membound or mtp):
+under profiles/ (run from /tmp, TMPDIR=/tmp; WL = membound, mtp, large,
+ragged or hkv2):
   rocprofv3 --kernel-trace --stats -d DIR/trace_WL -o run --output-format csv
-      -- python3 /root/repo/bench.py --workload WL --steps 100 --warmup 10 --no-cpu-baseline
+      -- python3 /root/repo/bench.py --workload WL --steps 100 --warmup 10 --no-cpu-baseline --no-torch-baseline --no-ceilings
   rocprofv3 --pmc FETCH_SIZE -d DIR/pmc_FETCH_SIZE_WL -o run --output-format csv
-      -- python3 /root/repo/bench.py --workload WL --steps 5 --warmup 2 --no-cpu-baseline
+      -- python3 /root/repo/bench.py --workload WL --steps 5 --warmup 2 --no-cpu-baseline --no-torch-baseline --no-ceilings
   (the same with WRITE_SIZE), and both counters once more with
       -- python3 /root/repo/bench.py --copy-calibration   (dirs pmc_FETCH_SIZE_copy, ...)
 """
@@ -80,7 +89,7 @@ def kernel_source_digest():
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "mla_decode_attention_split_amd", "csrc")
     for name in sorted(os.listdir(csrc)):
-        if name.endswith((".hip", ".hpp")):
+        if name.endswith((".hip", ".hpp")) and name != "ceiling.hip":
             with open(os.path.join(csrc, name), "rb") as f:
                 h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()[:16]
@@ -118,16 +127,20 @@ def cpu_baseline(w, min_seconds=10.0):
                       f"runs of {med:.3f} s, fp64"}
 
 
-def torch_baseline(w, q, kv, bt, out_ref, steps=10):
-    """Plain PyTorch on the GPU, for context: gather every sequence's pages
-    into a padded dense K (B, Nmax, 576), scores as one batched bf16 product,
-    masked softmax in fp32, P (bf16) times V.  One KV head only.  Every
-    operand of a bf16 batched product is made contiguous first."""
+def torch_baseline(w, q, kv, bt, steps=10):
+    """Plain PyTorch on the GPU, for context (the pages compare FlashMLA with a
+    native Torch implementation): gather every sequence's pages into a padded
+    dense K (B, Nmax, 576), scores as one batched 16-bit product, masked
+    softmax in fp32, P (rounded to q's type) times V.  One KV head only.
+    Every operand of a batched product is made contiguous first.
+
+    Returns (ms per call, out [B, s_q, h_q, 512] in q's type, lse fp32
+    [B, s_q, h_q])."""
     import torch
     B, s_q, h_q = w.batch, w.s_q, w.h_q
     M = s_q * h_q
     n = torch.from_numpy(w.seqlens.astype(np.int64)).to(q.device)
-    pmax = int((int(w.seqlens.max()) + 63) // 64)
+    pmax = max(1, int((int(w.seqlens.max()) + 63) // 64))
     jj = torch.arange(pmax * 64, device=q.device)
     row_t = torch.arange(M, device=q.device) // h_q
     lim = n[:, None] - s_q + row_t[None, :] + 1 if w.causal else n[:, None].expand(B, M)
@@ -141,11 +154,11 @@ def torch_baseline(w, q, kv, bt, out_ref, steps=10):
         St = torch.bmm(K, qT).float() * w.scale                            # (B, Nmax, M)
         St = St.masked_fill(masked, float("-inf"))
         lse = torch.logsumexp(St, dim=1)                                   # (B, M)
-        P = torch.exp(St - lse[:, None, :]).transpose(1, 2).contiguous().to(torch.bfloat16)
+        P = torch.exp(St - lse[:, None, :]).transpose(1, 2).contiguous().to(q.dtype)
         V = K[:, :, :512].contiguous()
         return torch.bmm(P, V), lse                                        # (B, M, 512)
 
-    o, _ = run()
+    o, l = run()
     torch.cuda.synchronize()
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
@@ -155,8 +168,7 @@ def torch_baseline(w, q, kv, bt, out_ref, steps=10):
     e1.record()
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / steps
-    diff = (o.float().reshape(B, s_q, h_q, 512) - out_ref.float()).abs().max().item()
-    return ms, diff
+    return ms, o.reshape(B, s_q, h_q, 512), l.reshape(B, s_q, h_q)
 
 
 def _csv_rows(path):
@@ -196,7 +208,7 @@ def summarize_profiles(d):
                                 "fetch_scale": round(cal["FETCH_SIZE"]["scale"], 4),
                                 "write_scale": round(cal["WRITE_SIZE"]["scale"], 4)},
                 "workloads": {}}
-    for wl in ("membound", "mtp", "large", "ragged"):
+    for wl in ("membound", "mtp", "large", "ragged", "hkv2"):
         tdir = os.path.join(d, f"trace_{wl}")
         if not os.path.isdir(tdir):
             continue
@@ -209,7 +221,7 @@ def summarize_profiles(d):
         lines = [f"# rocprofv3 kernel trace: paged MLA decode, workload {wl}", "",
                  "command (from /tmp, TMPDIR=/tmp):",
                  f"  rocprofv3 --kernel-trace --stats -d DIR/trace_{wl} -o run --output-format csv "
-                 f"-- python3 /root/repo/bench.py --workload {wl} --steps 100 --warmup 10 --no-cpu-baseline",
+                 f"-- python3 /root/repo/bench.py --workload {wl} --steps 100 --warmup 10 --no-cpu-baseline --no-torch-baseline --no-ceilings",
                  f"kernel source digest: {counters['kernel_source_digest']}", "",
                  f"{'kernel':60s} {'calls':>6s} {'avg us':>9s} {'min us':>9s} {'max us':>9s}"]
         for r in stats:
@@ -247,7 +259,7 @@ def summarize_profiles(d):
                       f"  command: rocprofv3 --pmc SQ_WAVES SQ_WAVE_CYCLES SQ_BUSY_CYCLES "
                       f"SQ_VALU_MFMA_BUSY_CYCLES SQ_LDS_BANK_CONFLICT SQ_INSTS_LDS SQ_WAIT_INST_ANY "
                       f"SQ_ACTIVE_INST_ANY GRBM_GUI_ACTIVE -d DIR/pmc_SQ_{wl} -o run --output-format csv -- "
-                      f"python3 /root/repo/bench.py --workload {wl} --steps 5 --warmup 2 --no-cpu-baseline"]
+                      f"python3 /root/repo/bench.py --workload {wl} --steps 5 --warmup 2 --no-cpu-baseline --no-torch-baseline --no-ceilings"]
             for k in sorted(mean):
                 lines.append(f"  {k:28s} {mean[k]:16.1f}")
             if mean.get("GRBM_GUI_ACTIVE") and "SQ_VALU_MFMA_BUSY_CYCLES" in mean:
@@ -284,20 +296,239 @@ def summarize_profiles(d):
     print(json.dumps(counters, indent=1))
 
 
+def ceiling_lib():
+    """The measurement library (libmla_ceiling.so, include/mla_ceiling.h)."""
+    global _CEILING
+    if _CEILING is None:
+        import ctypes
+        import mla_decode_attention_split_amd as mla
+        path = os.path.join(os.path.dirname(mla.library_path()), "libmla_ceiling.so")
+        if not os.path.exists(path):
+            raise RuntimeError(f"{path} is missing: build it with "
+                               "`python -m mla_decode_attention_split_amd.build`")
+        lib = ctypes.CDLL(path)
+        p, i = ctypes.c_void_p, ctypes.c_int
+        lib.mla_ceiling_stream.argtypes = [p, i, i, p, i, i, p, p]
+        lib.mla_ceiling_stream.restype = i
+        lib.mla_ceiling_mfma.argtypes = [p, i, i, p]
+        lib.mla_ceiling_mfma.restype = i
+        lib.mla_ceiling_last_error.restype = ctypes.c_char_p
+        _CEILING = lib
+    return _CEILING
+
+
+_CEILING = None
+
+
+def _ceiling_check(rc):
+    if rc != 0:
+        raise RuntimeError(f"ceiling probe failed [{rc}]: {ceiling_lib().mla_ceiling_last_error().decode()}")
+
+
+def _stream_ptr(t):
+    import torch
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def ceiling_stream(pool, pages, sink):
+    """Stream the cache pages listed in ``pages`` (int32 [workgroups,
+    pages_per_workgroup]) of ``pool`` ([num_pages, 64 * 576] 16-bit) through
+    the decode kernel's LDS ring, no arithmetic."""
+    W, P = pages.shape
+    _ceiling_check(ceiling_lib().mla_ceiling_stream(
+        pool.data_ptr(), int(pool.shape[0]), pool[0].numel() * pool.element_size(), pages.data_ptr(),
+        int(W), int(P), sink.data_ptr(), _stream_ptr(pool)))
+
+
+def ceiling_mfma(sink, num_workgroups, iters):
+    """num_workgroups x 4 waves of iters x 4 independent 32x32x16 bf16 MFMAs."""
+    _ceiling_check(ceiling_lib().mla_ceiling_mfma(sink.data_ptr(), int(num_workgroups), int(iters),
+                                                  _stream_ptr(sink)))
+
+
+def span_ms(fn, k, hold_cycles=int(2.4e9 * 0.005)):
+    """Mean duration of k back-to-back calls of fn(i), HIP events on the
+    current stream at both ends, the stream held by a spin while they are
+    enqueued."""
+    import torch
+    a0 = torch.cuda.Event(enable_timing=True)
+    a1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    torch.cuda._sleep(hold_cycles)
+    a0.record()
+    for i in range(k):
+        fn(i)
+    a1.record()
+    torch.cuda.synchronize()
+    return a0.elapsed_time(a1) / k
+
+
+def measure_workload(name, args, dev, primary):
+    """Time one workload's step and its parts; returns (block, w, out, lse)."""
+    import torch
+    import mla_decode_attention_split_amd as mla
+    from mla_decode_attention_split_amd import synth
+
+    w = synth.named_workload(name, dtype=args.dtype)
+    nbytes, flops = algorithmic_units(w)
+    M, h_kv = w.rows_per_kv_head, w.h_kv
+    pool_bytes = w.kcache.nbytes
+    copies = max(1, int(np.ceil(args.rotate_bytes / pool_bytes)))
+    eprint(f"[{name}] B={w.batch} s_q={w.s_q} h_q={w.h_q} h_kv={h_kv} causal={w.causal} "
+           f"sum(N)={int(w.seqlens.sum())} bytes={nbytes / 1e6:.2f} MB flops={flops / 1e9:.2f} GFLOP "
+           f"pool={pool_bytes / 1e6:.1f} MB x{copies} copies")
+
+    tdt = torch.float16 if args.dtype == "fp16" else torch.bfloat16
+    q = torch.from_numpy(w.q.view(np.int16)).to(dev).view(tdt)
+    kv0 = torch.from_numpy(w.kcache.view(np.int16)).to(dev).view(tdt)
+    kvs = [kv0] + [kv0.clone() for _ in range(copies - 1)]
+    bt = torch.from_numpy(np.ascontiguousarray(w.block_table)).to(dev)
+    sl = torch.from_numpy(np.ascontiguousarray(w.seqlens)).to(dev)
+    num_parts, _ = mla.mla_metadata_shape(w.batch, M, h_kv)
+    tile_rows, m_tiles, fixed_cost = mla.mla_tile_shape(M, h_kv)
+    meta = torch.empty((num_parts, 8), dtype=torch.int32, device=dev)
+    splits = torch.empty((w.batch + 1,), dtype=torch.int32, device=dev)
+    out = torch.empty((w.batch, w.s_q, w.h_q, 512), dtype=tdt, device=dev)
+    lse = torch.empty((w.batch, w.s_q, w.h_q), dtype=torch.float32, device=dev)
+    ws = torch.empty((mla.mla_workspace_bytes(w.batch, M, h_kv, num_parts),), dtype=torch.uint8,
+                     device=dev)
+    eprint(f"[{name}] num_parts={num_parts} fixed_cost={fixed_cost} tile_rows={tile_rows} "
+           f"grid={num_parts * m_tiles * h_kv}")
+
+    def step(i):
+        mla.mla_get_metadata(sl, M, h_kv, tile_metadata=meta, num_splits=splits)
+        mla.mla_decode_splitkv(q, kvs[i % copies], bt, sl, meta, splits, causal=w.causal,
+                               softmax_scale=w.scale, out=out, lse=lse, workspace=ws)
+        mla.mla_decode_combine(splits, out, lse, ws, num_parts=num_parts, h_kv=h_kv)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    # Host enqueue rate, to size the spin that holds the stream while the
+    # timed steps are queued (so the GPU then runs them back to back).
+    t0 = time.perf_counter()
+    for i in range(20):
+        step(i)
+    enqueue_s = (time.perf_counter() - t0) / 20
+    torch.cuda.synchronize()
+    hold_cycles = int(2.4e9 * (1.5 * enqueue_s * args.steps + 0.01))
+
+    # Pass 1: throughput of whole steps (events only at the ends).
+    ms_per_step = span_ms(step, args.steps, hold_cycles)
+
+    # The timed step's result, checked bitwise against one mla_decode call on
+    # the same inputs (the two launches of the step are the decode's halves).
+    step(0)
+    out_chk = torch.empty_like(out)
+    lse_chk = torch.empty_like(lse)
+    mla.mla_decode(q, kvs[0], bt, sl, meta, splits, causal=w.causal, softmax_scale=w.scale,
+                   out=out_chk, lse=lse_chk)
+    torch.cuda.synchronize()
+    same = bool(torch.equal(out.view(torch.int16), out_chk.view(torch.int16)) and
+                torch.equal(lse.view(torch.int32), lse_chk.view(torch.int32)))
+    out_np = out.float().cpu().numpy().astype(np.float64)
+    lse_np = lse.cpu().numpy().astype(np.float64)
+
+    # Pass 2: the main kernel alone, launched back to back over the same
+    # metadata (computed once, outside the timed region), HIP events at both
+    # ends on the stream the kernel runs on; mean launch duration = span / K.
+    dec_ms = span_ms(lambda i: mla.mla_decode_splitkv(q, kvs[i % copies], bt, sl, meta, splits,
+                                                      causal=w.causal, softmax_scale=w.scale,
+                                                      out=out, lse=lse, workspace=ws),
+                     args.steps, hold_cycles)
+    # Pass 3: the metadata call and the combine alone (same buffers).
+    meta_ms = span_ms(lambda i: mla.mla_get_metadata(sl, M, h_kv, tile_metadata=meta,
+                                                     num_splits=splits), 200)
+    comb_ms = span_ms(lambda i: mla.mla_decode_combine(splits, out, lse, ws, num_parts=num_parts,
+                                                       h_kv=h_kv), 200)
+
+    hbm_bound = name != "mtp"
+    step_tbs = nbytes / (ms_per_step * 1e-3) / 1e12
+    step_tflops = flops / (ms_per_step * 1e-3) / 1e12
+    if hbm_bound:
+        achieved = nbytes / (dec_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4)}
+    else:
+        achieved = flops / (dec_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4)}
+    roof["traffic"] = counter_traffic(name)
+    eprint(f"[{name}] host enqueue {enqueue_s * 1e6:.1f} us/step")
+    eprint(f"[{name}] step {ms_per_step * 1e3:.2f} us -> {step_tbs:.3f} TB/s, {step_tflops:.1f} TFLOP/s")
+    eprint(f"[{name}] decode kernel {dec_ms * 1e3:.2f} us mean over {args.steps} back-to-back launches "
+           f"-> {achieved:.1f} {roof['unit']} ({roof['frac'] * 100:.1f}% of peak)")
+    eprint(f"[{name}] metadata call {meta_ms * 1e3:.2f} us, combine {comb_ms * 1e3:.2f} us (each alone); "
+           f"timed step equals mla_decode bitwise: {same}")
+
+    block = {
+        "workload": name,
+        "config": {"workload": w.name, "batch": w.batch, "s_q": w.s_q, "h_q": w.h_q,
+                   "h_kv": h_kv, "seqlens_sum": int(w.seqlens.sum()), "page": 64, "d": 576,
+                   "dv": 512, "causal": bool(w.causal), "kv_pool_copies": copies,
+                   "num_parts": num_parts, "tile_rows": tile_rows},
+        "ms_per_step": round(ms_per_step, 5),
+        "tbs": round(step_tbs, 4),
+        "tflops": round(step_tflops, 3),
+        "decode_kernel_us": round(dec_ms * 1e3, 3),
+        "roofline": roof,
+        "parts_us": {"metadata": round(meta_ms * 1e3, 3), "decode": round(dec_ms * 1e3, 3),
+                     "combine": round(comb_ms * 1e3, 3)},
+        "step_equals_mla_decode": same,
+    }
+    if not args.no_torch_baseline and h_kv == 1:
+        t_ms, t_out, _ = torch_baseline(w, q, kvs[0], bt)
+        t_diff = float((t_out.float().reshape(out_chk.shape) - out_chk.float()).abs().max().item())
+        block["gpu_torch_baseline"] = {
+            "value": round(nbytes / (t_ms * 1e-3) / 1e12, 4), "unit": "TB/s",
+            "tflops": round(flops / (t_ms * 1e-3) / 1e12, 2), "ms": round(t_ms, 4),
+            "max_abs_diff_vs_kernel": t_diff,
+            "what": "PyTorch on the GPU: padded dense gather of the pages, bf16 batched products, "
+                    "fp32 masked softmax; pool already warm in cache"}
+        eprint(f"[{name}] torch baseline {t_ms * 1e3:.1f} us per call "
+               f"({nbytes / (t_ms * 1e-3) / 1e12:.3f} TB/s, {flops / (t_ms * 1e-3) / 1e12:.1f} TFLOP/s), "
+               f"max |diff| vs kernel {t_diff:.3g}")
+        del t_out
+    ctx = {"w": w, "kvs": kvs, "hbm_bound": hbm_bound, "achieved": achieved, "nbytes": nbytes,
+           "flops": flops, "out": out_np, "lse": lse_np, "copies": copies}
+    return block, ctx
+
+
+def oracle_parity(ctx):
+    """The GPU step's whole out / lse against the oracle (test infrastructure),
+    with the tolerance the tests use."""
+    import oracle
+    w = ctx["w"]
+    ro, rl = oracle.decode(w.q, w.kcache, w.block_table, w.seqlens, causal=w.causal, scale=w.scale,
+                           dtype=w.dtype)
+    d = ctx["out"] - ro
+    fin = np.isfinite(rl)
+    res = {"out_max_abs": float(np.abs(d).max()),
+           "out_rel_fro": float(np.linalg.norm(d) / max(np.linalg.norm(ro), 1e-300)),
+           "lse_max_abs": float(np.abs(ctx["lse"][fin] - rl[fin]).max()) if fin.any() else 0.0}
+    res["within_tolerance"] = bool(res["out_max_abs"] <= 2e-2 and res["out_rel_fro"] <= 5e-3 and
+                                   res["lse_max_abs"] <= 1e-3)
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=500)
     ap.add_argument("--warmup", type=int, default=50)
-    ap.add_argument("--workload", default="membound",
-                    choices=["tiny", "membound", "mtp", "large", "ragged", "hkv2"])
+    ap.add_argument("--workload", default=None,
+                    choices=["tiny", "membound", "mtp", "large", "ragged", "hkv2"],
+                    help="measure only this workload (default: membound, plus mtp as the "
+                         "compute-bound half of the metric)")
     ap.add_argument("--dtype", default="bf16", choices=["bf16", "fp16"],
                     help="element type of q, the cache and out")
     ap.add_argument("--rotate-bytes", type=float, default=float(1 << 30),
                     help="total bytes of KV pool copies the steps rotate over")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--torch-baseline", action="store_true",
-                    help="also time a plain PyTorch implementation on the GPU (context)")
+    ap.add_argument("--no-cpu-baseline", action="store_true",
+                    help="skip the oracle (CPU baseline timing and the parity check)")
+    ap.add_argument("--no-torch-baseline", action="store_true",
+                    help="skip the plain PyTorch implementation on the GPU (context)")
+    ap.add_argument("--no-ceilings", action="store_true", help="skip the measured ceilings")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (to scale HBM counters)")
     ap.add_argument("--summarize-profiles", metavar="DIR",
@@ -330,206 +561,94 @@ def main():
         eprint(f"copied {n} bytes x 5")
         return
 
-    import mla_decode_attention_split_amd as mla
-    from mla_decode_attention_split_amd import synth
+    primary_name = args.workload or "membound"
+    block, ctx = measure_workload(primary_name, args, dev, primary=True)
+    second = None
+    if args.workload is None:
+        second, ctx2 = measure_workload("mtp", args, dev, primary=False)
 
-    w = synth.named_workload(args.workload, dtype=args.dtype)
-    nbytes, flops = algorithmic_units(w)
-    M, h_kv = w.rows_per_kv_head, w.h_kv
-    pool_bytes = w.kcache.nbytes
-    copies = max(1, int(np.ceil(args.rotate_bytes / pool_bytes)))
-    eprint(f"workload {w.name}: B={w.batch} s_q={w.s_q} h_q={w.h_q} h_kv={h_kv} "
-           f"causal={w.causal} sum(N)={int(w.seqlens.sum())} bytes={nbytes / 1e6:.2f} MB "
-           f"flops={flops / 1e9:.2f} GFLOP pool={pool_bytes / 1e6:.1f} MB x{copies} copies")
+    # Ceilings measured on this GPU: (a) the pages the primary workload reads,
+    # streamed through the main kernel's LDS ring with no arithmetic, over the
+    # same rotating pool copies; (b) a loop of independent bf16 MFMAs on every
+    # SIMD.
+    ceilings = None
+    if not args.no_ceilings:
+        w = ctx["w"]
+        used = [p for b in range(w.batch) for p in w.block_table[b, :(int(w.seqlens[b]) + 63) // 64]]
+        groups = 256
+        per = max(1, (len(used) + groups - 1) // groups)
+        plist = np.full(groups * per, w.kcache.shape[0], dtype=np.int32)  # padding: outside the pool
+        plist[:len(used)] = np.asarray(used, dtype=np.int32)
+        pages_t = torch.from_numpy(plist.reshape(groups, per)).to(dev)
+        isink = torch.zeros(1, dtype=torch.int32, device=dev)
+        fsink = torch.zeros(1, dtype=torch.float32, device=dev)
+        stream_tbs = None
+        if w.h_kv == 1:  # the ring streams pages of one KV head
+            kv_pages = [kc.view(kc.shape[0], -1) for kc in ctx["kvs"]]
+            copies = ctx["copies"]
+            for i in range(3):
+                ceiling_stream(kv_pages[i % copies], pages_t, isink)
+            stream_ms = span_ms(lambda i: ceiling_stream(kv_pages[i % copies], pages_t, isink), 100)
+            stream_tbs = len(used) * 64 * 1152 / (stream_ms * 1e-3) / 1e12
+        mf_wg, mf_it = 1024, 1000
+        ceiling_mfma(fsink, mf_wg, mf_it)
+        mfma_ms = span_ms(lambda i: ceiling_mfma(fsink, mf_wg, mf_it), 20)
+        mfma_tflops = mf_wg * 4 * mf_it * 4 * 32768 / (mfma_ms * 1e-3) / 1e12
+        ceilings = {
+            "stream_read": None if stream_tbs is None else {
+                "value": round(stream_tbs, 4), "unit": "TB/s",
+                "what": f"the {primary_name} workload's cache pages through the main kernel's LDS "
+                        f"ring, no arithmetic, rotating pool copies"},
+            "mfma_bf16": {"value": round(mfma_tflops, 1), "unit": "TFLOP/s",
+                          "what": "independent 32x32x16 bf16 MFMA chains on every SIMD"},
+        }
+        ceil_p = (stream_tbs * 1e3 if stream_tbs else None) if ctx["hbm_bound"] else mfma_tflops
+        ceilings["decode_frac"] = round(ctx["achieved"] / ceil_p, 4) if ceil_p else None
+        if second is not None:
+            ceilings["compute_bound_decode_frac"] = round(ctx2["achieved"] / mfma_tflops, 4)
+        eprint(f"measured ceilings: paged stream {stream_tbs} TB/s, bf16 MFMA loop {mfma_tflops:.1f} TFLOP/s")
+        for key, c in (("primary", ctx), ("compute-bound", ctx2 if second is not None else None)):
+            if c is not None:
+                cp = (stream_tbs * 1e3 if stream_tbs else None) if c["hbm_bound"] else mfma_tflops
+                if cp:
+                    eprint(f"{key} decode kernel at {c['achieved'] / cp * 100:.1f}% of the measured "
+                           f"{'stream' if c['hbm_bound'] else 'MFMA'} ceiling")
 
-    tdt = torch.float16 if args.dtype == "fp16" else torch.bfloat16
-    q = torch.from_numpy(w.q.view(np.int16)).to(dev).view(tdt)
-    kv0 = torch.from_numpy(w.kcache.view(np.int16)).to(dev).view(tdt)
-    kvs = [kv0] + [kv0.clone() for _ in range(copies - 1)]
-    bt = torch.from_numpy(np.ascontiguousarray(w.block_table)).to(dev)
-    sl = torch.from_numpy(np.ascontiguousarray(w.seqlens)).to(dev)
-    num_parts, fixed_cost, tile_rows = mla.mla_get_metadata_shape(w.batch, M, h_kv)
-    meta = torch.empty((num_parts, 8), dtype=torch.int32, device=dev)
-    splits = torch.empty((w.batch + 1,), dtype=torch.int32, device=dev)
-    out = torch.empty((w.batch, w.s_q, w.h_q, 512), dtype=tdt, device=dev)
-    lse = torch.empty((w.batch, w.s_q, w.h_q), dtype=torch.float32, device=dev)
-    ws = torch.empty((mla.mla_decode_workspace_size(w.batch, M, h_kv, num_parts),),
-                     dtype=torch.uint8, device=dev)
-    eprint(f"num_parts={num_parts} fixed_cost={fixed_cost} tile_rows={tile_rows} "
-           f"grid={num_parts * ((M + tile_rows - 1) // tile_rows) * h_kv}")
-
-    def step(i):
-        mla.mla_get_metadata(sl, M, h_kv, num_parts=num_parts, fixed_cost=fixed_cost,
-                             tile_metadata=meta, num_splits=splits)
-        mla.mla_decode_splitkv(q, kvs[i % copies], bt, sl, meta, splits, causal=w.causal,
-                               softmax_scale=w.scale, out=out, lse=lse, workspace=ws)
-        mla.mla_decode_combine(splits, out, lse, ws, num_parts=num_parts, h_kv=h_kv)
-
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-    # Host enqueue rate, to size the spin that holds the stream while the
-    # timed steps are queued (so the GPU then runs them back to back).
-    t0 = time.perf_counter()
-    for i in range(20):
-        step(i)
-    enqueue_s = (time.perf_counter() - t0) / 20
-    torch.cuda.synchronize()
-    hold_cycles = int(2.4e9 * (1.5 * enqueue_s * args.steps + 0.01))
-
-    # Pass 1: throughput of whole steps (events only at the ends).
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    torch.cuda._sleep(hold_cycles)
-    t0 = time.perf_counter()
-    e0.record()
-    for i in range(args.steps):
-        step(i)
-    e1.record()
-    t_enq = time.perf_counter() - t0
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_per_step = e0.elapsed_time(e1) / args.steps
-
-    # Pass 2: the main kernel alone, launched back to back over the same
-    # metadata (computed once, outside the timed region), HIP events at both
-    # ends on the stream the kernel runs on; mean launch duration = span / K.
-    step(0)
-    torch.cuda.synchronize()
-    d0 = torch.cuda.Event(enable_timing=True)
-    d1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda._sleep(hold_cycles)
-    d0.record()
-    for i in range(args.steps):
-        mla.mla_decode_splitkv(q, kvs[i % copies], bt, sl, meta, splits, causal=w.causal,
-                               softmax_scale=w.scale, out=out, lse=lse, workspace=ws)
-    d1.record()
-    torch.cuda.synchronize()
-    dec_mean_ms = d0.elapsed_time(d1) / args.steps
-
-    # Pass 3: the metadata call and the combine alone (same buffers), so the
-    # step's parts are reported separately.
-    def span_ms(fn, k):
-        a0 = torch.cuda.Event(enable_timing=True)
-        a1 = torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        torch.cuda._sleep(int(2.4e9 * 0.005))
-        a0.record()
-        for i in range(k):
-            fn(i)
-        a1.record()
-        torch.cuda.synchronize()
-        return a0.elapsed_time(a1) / k
-
-    meta_ms = span_ms(lambda i: mla.mla_get_metadata(sl, M, h_kv, num_parts=num_parts,
-                                                     fixed_cost=fixed_cost, tile_metadata=meta,
-                                                     num_splits=splits), 200)
-    comb_ms = span_ms(lambda i: mla.mla_decode_combine(splits, out, lse, ws, num_parts=num_parts,
-                                                       h_kv=h_kv), 200)
-
-    # Pass 4: ceilings measured on this GPU.  (a) The pages this workload
-    # reads, streamed through the main kernel's LDS ring with no arithmetic,
-    # over the same rotating pool copies; (b) a loop of independent bf16
-    # MFMAs on every SIMD.
-    used = [p for b in range(w.batch) for p in w.block_table[b, :(int(w.seqlens[b]) + 63) // 64]]
-    groups = 256
-    per = max(1, (len(used) + groups - 1) // groups)
-    plist = np.full(groups * per, w.kcache.shape[0], dtype=np.int32)  # padding: outside the pool
-    plist[:len(used)] = np.asarray(used, dtype=np.int32)
-    pages_t = torch.from_numpy(plist.reshape(groups, per)).to(dev)
-    isink = torch.zeros(1, dtype=torch.int32, device=dev)
-    fsink = torch.zeros(1, dtype=torch.float32, device=dev)
-    stream_tbs = None
-    if h_kv == 1:  # the ring streams pages of one KV head
-        kv_pages = [kc.view(kc.shape[0], -1) for kc in kvs]
-        for i in range(3):
-            mla.mla_ceiling_stream(kv_pages[i % copies], pages_t, isink)
-        stream_ms = span_ms(lambda i: mla.mla_ceiling_stream(kv_pages[i % copies], pages_t, isink), 100)
-        stream_tbs = len(used) * 64 * 1152 / (stream_ms * 1e-3) / 1e12
-    mf_wg, mf_it = 1024, 1000
-    mla.mla_ceiling_mfma(fsink, mf_wg, mf_it)
-    mfma_ms = span_ms(lambda i: mla.mla_ceiling_mfma(fsink, mf_wg, mf_it), 20)
-    mfma_tflops = mf_wg * 4 * mf_it * 4 * 32768 / (mfma_ms * 1e-3) / 1e12
-
-    value_tbs = nbytes / (ms_per_step * 1e-3) / 1e12
-    hbm_bound = args.workload != "mtp"
-    if hbm_bound:
-        achieved = nbytes / (dec_mean_ms * 1e-3) / 1e9
-        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4)}
-    else:
-        achieved = flops / (dec_mean_ms * 1e-3) / 1e12
-        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4)}
-    traffic = counter_traffic(args.workload)
-    roof["traffic"] = traffic
-
-    eprint(f"host enqueue {enqueue_s * 1e6:.1f} us/step, timed loop enqueued in {t_enq * 1e3:.1f} ms "
-           f"behind a {hold_cycles / 2.4e6:.1f} ms hold")
-    eprint(f"step {ms_per_step * 1e3:.2f} us (wall incl. hold {wall / args.steps * 1e6:.2f} us)  "
-           f"-> {value_tbs:.3f} TB/s, {flops / (ms_per_step * 1e-3) / 1e12:.1f} TFLOP/s")
-    eprint(f"decode kernel {dec_mean_ms * 1e3:.2f} us mean over {args.steps} back-to-back launches "
-           f"-> {achieved:.1f} {roof['unit']} "
-           f"({roof['frac'] * 100:.1f}% of peak)")
-    ceil_val = (stream_tbs * 1e3 if stream_tbs else None) if hbm_bound else mfma_tflops
-    eprint(f"metadata call {meta_ms * 1e3:.2f} us, combine {comb_ms * 1e3:.2f} us (each alone)")
-    if stream_tbs:
-        eprint(f"measured ceilings: paged stream {stream_tbs:.3f} TB/s ({len(used)} pages, "
-               f"{stream_ms * 1e3:.2f} us), bf16 MFMA loop {mfma_tflops:.1f} TFLOP/s")
-    else:
-        eprint(f"measured ceilings: bf16 MFMA loop {mfma_tflops:.1f} TFLOP/s (stream ceiling: one KV head only)")
-    if ceil_val:
-        eprint(f"decode kernel at {achieved / ceil_val * 100:.1f}% of the measured "
-               f"{'stream' if hbm_bound else 'MFMA'} ceiling")
-
+    hbm_bound = ctx["hbm_bound"]
     result = {
         "metric": METRIC,
-        "value": round(value_tbs, 4) if hbm_bound else round(flops / (ms_per_step * 1e-3) / 1e12, 2),
+        "value": block["tbs"] if hbm_bound else block["tflops"],
         "unit": "TB/s" if hbm_bound else "TFLOP/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 5),
+        "ms_per_step": block["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": args.dtype,
         "data": "synthetic",
-        "config": {"workload": w.name, "batch": w.batch, "s_q": w.s_q, "h_q": w.h_q,
-                   "h_kv": h_kv, "seqlens_sum": int(w.seqlens.sum()), "page": 64, "d": 576,
-                   "dv": 512, "causal": bool(w.causal), "kv_pool_copies": copies,
-                   "num_parts": num_parts},
-        "tflops": round(flops / (ms_per_step * 1e-3) / 1e12, 3),
-        "decode_kernel_us": round(dec_mean_ms * 1e3, 3),
-        "roofline": roof,
-        "parts_us": {"metadata": round(meta_ms * 1e3, 3), "decode": round(dec_mean_ms * 1e3, 3),
-                     "combine": round(comb_ms * 1e3, 3)},
-        "measured_ceilings": {
-            "stream_read": None if stream_tbs is None else {"value": round(stream_tbs, 4), "unit": "TB/s",
-                            "what": "the workload's cache pages through the main kernel's LDS "
-                                    "ring, no arithmetic, rotating pool copies"},
-            "mfma_bf16": {"value": round(mfma_tflops, 1), "unit": "TFLOP/s",
-                          "what": "independent 32x32x16 bf16 MFMA chains on every SIMD"},
-            "decode_frac": round(achieved / ceil_val, 4) if ceil_val else None,
-        },
+        "config": block["config"],
+        "tflops": block["tflops"],
+        "decode_kernel_us": block["decode_kernel_us"],
+        "roofline": block["roofline"],
+        "parts_us": block["parts_us"],
+        "step_equals_mla_decode": block["step_equals_mla_decode"],
     }
-    if args.torch_baseline and h_kv == 1:
-        step(0)
-        torch.cuda.synchronize()
-        t_ms, t_diff = torch_baseline(w, q, kvs[0], bt, out)
-        result["gpu_torch_baseline"] = {
-            "value": round(nbytes / (t_ms * 1e-3) / 1e12, 4), "unit": "TB/s",
-            "tflops": round(flops / (t_ms * 1e-3) / 1e12, 2), "ms": round(t_ms, 4),
-            "max_abs_diff_vs_kernel": t_diff,
-            "what": "PyTorch on the GPU: padded dense gather of the pages, bf16 batched products, "
-                    "fp32 masked softmax; pool already warm in cache"}
-        eprint(f"torch baseline {t_ms * 1e3:.1f} us per call ({nbytes / (t_ms * 1e-3) / 1e12:.3f} TB/s), "
-               f"max |diff| vs kernel {t_diff:.3g}")
+    if "gpu_torch_baseline" in block:
+        result["gpu_torch_baseline"] = block["gpu_torch_baseline"]
+    if second is not None:
+        result["compute_bound"] = second
+    if ceilings is not None:
+        result["measured_ceilings"] = ceilings
     if not args.no_cpu_baseline:
         eprint("cpu baseline (oracle) ...")
-        result["cpu_baseline"] = cpu_baseline(w)
+        result["cpu_baseline"] = cpu_baseline(ctx["w"])
         eprint(f"cpu baseline {result['cpu_baseline']}")
+        result["oracle_parity"] = {primary_name: oracle_parity(ctx)}
+        if second is not None:
+            result["oracle_parity"]["mtp"] = oracle_parity(ctx2)
+        eprint(f"oracle parity {result['oracle_parity']}")
     print(json.dumps(result), flush=True)
 
 

@@ -3,14 +3,18 @@
  * MI355X (gfx950).
  *
  * The operation (pages on FlashMLA):
- *   - "DeepSeek 开源记-第1天-FlashMLA", section 6 (使用方法): two calls,
- *       tile_scheduler_metadata, num_splits = get_mla_metadata(cache_seqlens,
- *           s_q * h_q // h_kv, h_kv)
- *       output, lse = flash_mla_with_kvcache(q, blocked_k, block_table,
- *           cache_seqlens, dv, tile_scheduler_metadata, num_splits, causal)
- *     section 2 (核心功能): head dim fixed at 576, value dim fixed at 512,
- *     Shared-KV (V is the first 512 dims of the cached 576-wide row);
- *     section 4 (核心实现): blockwise scores, softmax, merge of partial outputs.
+ *   - "DeepSeek 开源记-第1天-FlashMLA" (cnblogs), section 6 (使用方法): the
+ *     library is driven by two calls.  The first turns the per-sequence cache
+ *     lengths, the query rows per KV head (s_q * h_q / h_kv) and the KV head
+ *     count into scheduling metadata plus a per-sequence split count; the
+ *     second runs the decode over the paged cache with the query, the block
+ *     table, the cache lengths, the value dim, that metadata and a causal
+ *     flag, and gives back the output and its log-sum-exp.  Here they are
+ *     mla_get_metadata and mla_decode.
+ *     Section 2 (核心功能): head dim fixed at 576, value dim fixed at 512,
+ *     Shared-KV (V is the first 512 dims of the cached 576-wide row).
+ *     Section 4 (核心实现): blockwise scores, softmax, merge of partial
+ *     outputs.
  *   - "DeepSeek代碼開源第一彈Flash MLA" (ygpos news): BF16 and a paged KV cache
  *     with block size 64; variable-length sequences.
  *   - FlashMLA explainer (jsxs2.com), section 3.1: the work is cut into small
@@ -40,9 +44,9 @@
  *   - Preconditions only the device could check (they are not checked):
  *     block_table entries for blocks below ceil(N/64) are valid page indices
  *     in [0, num_pages); ceil(N/64) <= max_blocks_per_seq; the metadata was
- *     produced by mla_get_metadata for the same cache_seqlens, rows and h_kv.
- *     Cache rows at positions >= N and table entries >= ceil(N/64) are never
- *     used and may hold anything (NaN included).
+ *     produced by mla_get_metadata(_ex) for the same cache_seqlens, rows and
+ *     h_kv.  Cache rows at positions >= N and table entries >= ceil(N/64) are
+ *     never used and may hold anything (NaN included).
  */
 #ifndef MLA_DECODE_H
 #define MLA_DECODE_H
@@ -57,15 +61,15 @@ extern "C" {
 #define MLA_OK 0
 #define MLA_ERR_INVALID_ARG (-1) /* null pointer, bad size, misaligned buffer */
 #define MLA_ERR_UNSUPPORTED (-2) /* d != 576, dv != 512, page size != 64, ... */
-#define MLA_ERR_WORKSPACE (-3)   /* workspace smaller than mla_decode_workspace_size() */
+#define MLA_ERR_WORKSPACE (-3)   /* workspace smaller than mla_workspace_bytes() */
 #define MLA_ERR_HIP (-4)         /* a HIP runtime call or kernel launch failed */
 
 #define MLA_HEAD_DIM 576
 #define MLA_VALUE_DIM 512
 #define MLA_PAGE_SIZE 64
-/* Element type of q, blocked_k and out (one of the pages lists FP16 beside
- * BF16; the others BF16 only).  The arithmetic is the same: products of the
- * 16-bit inputs accumulated in fp32. */
+/* Element type of q, blocked_k and out (the cnblogs page, section 2, lists
+ * FP16 beside BF16; the others BF16 only).  The arithmetic is the same:
+ * products of the 16-bit inputs accumulated in fp32. */
 #define MLA_DTYPE_BF16 0
 #define MLA_DTYPE_FP16 1
 #define MLA_METADATA_WORDS 8   /* int32 words per part in tile_metadata */
@@ -80,22 +84,31 @@ const char *mla_status_string(int status);
 const char *mla_last_error(void);
 
 /*
- * Host-only sizing for get_mla_metadata (section 6 of the cnblogs page: the
- * second argument is s_q * h_q // h_kv).  Reads the current device's compute
- * unit count (cached) and touches no device memory.
+ * Host-only sizing of call 1 (the cnblogs page, section 6: the metadata call
+ * takes the query rows per KV head, s_q * h_q / h_kv, and h_kv).  Reads the
+ * current device's compute unit count (cached) and touches no device memory.
  *   q_rows_per_kv_head  M = s_q * h_q / h_kv, 1 <= M <= MLA_MAX_ROWS
- *   num_parts     out: number of parts the keys are partitioned into (the
- *                      decode grid is num_parts x ceil(M / tile_rows) x h_kv)
- *   fixed_cost    out: per-sequence overhead of the partition rule, in
- *                      32-key units (see mla_get_metadata)
- *   tile_rows     out: query rows per workgroup tile chosen for this M
- * Any out pointer may be NULL.
+ *   num_parts       out: parts mla_get_metadata partitions the keys into
+ *                        (the decode grid is num_parts x ceil(M / tile_rows)
+ *                        x h_kv workgroups)
+ *   words_per_part  out: MLA_METADATA_WORDS; tile_metadata is
+ *                        int32 [num_parts, words_per_part]
+ * Either out pointer may be NULL.
  */
-int mla_get_metadata_shape(int batch, int q_rows_per_kv_head, int h_kv, int *num_parts,
-                           int *fixed_cost, int *tile_rows);
+int mla_metadata_shape(int batch, int q_rows_per_kv_head, int h_kv, int *num_parts,
+                       int *words_per_part);
 
 /*
- * Call 1: split-KV scheduling metadata (the pages' get_mla_metadata).
+ * Host-only: the row tile the decode kernel uses for M rows per KV head
+ * (16, 32, 64 or 128 query rows per workgroup), the number of row tiles
+ * ceil(M / tile_rows), and the partition rule's default per-sequence cost
+ * in 32-key units (see mla_get_metadata).  Any out pointer may be NULL.
+ */
+int mla_tile_shape(int q_rows_per_kv_head, int h_kv, int *tile_rows, int *m_tiles,
+                   int *fixed_cost);
+
+/*
+ * Call 1: split-KV scheduling metadata (the pages' metadata call).
  * One device kernel (one workgroup) reads cache_seqlens and writes the
  * partition; nothing is copied to the host.
  *
@@ -104,13 +117,13 @@ int mla_get_metadata_shape(int batch, int q_rows_per_kv_head, int h_kv, int *num
  *   T = ceil(C_B / num_parts).  Unit i of sequence b belongs to part
  *   floor((C_b + fixed_cost + i) / T); a sequence with N_b = 0 gets one empty
  *   piece in part floor((C_b + fixed_cost - 1) / T).  A piece is the run of
- *   one sequence's units inside one part.
+ *   one sequence's units inside one part.  num_parts and fixed_cost are the
+ *   values mla_metadata_shape and mla_tile_shape report.
  *
  *   cache_seqlens  device int32 [batch], every N_b >= 0 (not checked on host)
- *   num_parts      1 <= num_parts <= MLA_MAX_PARTS (normally from
- *                  mla_get_metadata_shape; other values are allowed)
- *   fixed_cost     >= 1
- *   tile_metadata  device int32 [num_parts, MLA_METADATA_WORDS]: per part
+ *   batch          in [1, MLA_MAX_BATCH]
+ *   tile_metadata  device int32 [num_parts, MLA_METADATA_WORDS], 16-byte
+ *                  aligned: per part
  *                  {bb = first sequence, first key of its piece,
  *                   be = last sequence, end key (exclusive) of its piece,
  *                   num_splits[bb] + split index of bb's piece (the partial
@@ -119,18 +132,29 @@ int mla_get_metadata_shape(int batch, int q_rows_per_kv_head, int h_kv, int *num
  *                  an empty part stores {0, 0, -1, 0, 0, 0, 0, 0}
  *   num_splits     device int32 [batch + 1]: num_splits[0] = 0 and
  *                  num_splits[b+1] - num_splits[b] = pieces of sequence b
- * batch must be in [1, MLA_MAX_BATCH].
  */
 int mla_get_metadata(const int32_t *cache_seqlens, int batch, int q_rows_per_kv_head, int h_kv,
-                     int num_parts, int fixed_cost, int32_t *tile_metadata, int32_t *num_splits,
-                     void *stream);
-
-/* Bytes of device workspace mla_decode needs (fp32 partial outputs and
- * their lse for up to batch + num_parts pieces); 0 on invalid arguments. */
-size_t mla_decode_workspace_size(int batch, int q_rows_per_kv_head, int h_kv, int num_parts);
+                     int32_t *tile_metadata, int32_t *num_splits, void *stream);
 
 /*
- * Call 2: paged MLA decode (the pages' flash_mla_with_kvcache).
+ * mla_get_metadata with the partition's two parameters overridable (a hook
+ * for tests and tuning): num_parts_override in [1, MLA_MAX_PARTS] replaces
+ * the default part count (tile_metadata must then hold num_parts_override
+ * rows, and mla_decode gets num_parts = num_parts_override);
+ * fixed_cost_override >= 1 replaces the default per-sequence cost.  0 means
+ * the default for either.
+ */
+int mla_get_metadata_ex(const int32_t *cache_seqlens, int batch, int q_rows_per_kv_head, int h_kv,
+                        int32_t *tile_metadata, int32_t *num_splits, void *stream,
+                        int num_parts_override, int fixed_cost_override);
+
+/* Bytes of device workspace mla_decode needs (fp32 partial outputs and
+ * their lse for up to batch + num_parts pieces); 0 on invalid arguments
+ * (including dv != 512). */
+size_t mla_workspace_bytes(int batch, int q_rows_per_kv_head, int h_kv, int num_parts, int dv);
+
+/*
+ * Call 2: paged MLA decode (the pages' decode call).
  *   q              device [batch, s_q, h_q, 576] of dtype, 16-byte aligned
  *   blocked_k      device [num_pages, 64, h_kv, 576] of dtype, 16-byte aligned
  *   block_table    device int32 [batch, max_blocks_per_seq]
@@ -139,7 +163,7 @@ size_t mla_decode_workspace_size(int batch, int q_rows_per_kv_head, int h_kv, in
  *   dtype          MLA_DTYPE_BF16 or MLA_DTYPE_FP16 (else MLA_ERR_UNSUPPORTED):
  *                  the element type of q, blocked_k and out
  *   h_q % h_kv == 0; M = s_q * h_q / h_kv <= MLA_MAX_ROWS
- *   tile_metadata, num_parts, num_splits  from mla_get_metadata with
+ *   tile_metadata, num_parts, num_splits  from mla_get_metadata(_ex) with
  *                  q_rows_per_kv_head = M and the same h_kv
  *   causal         0/1: query t sees keys j <= N - s_q + t
  *   softmax_scale  multiplies the scores; positive and finite (the usual value
@@ -147,8 +171,8 @@ size_t mla_decode_workspace_size(int batch, int q_rows_per_kv_head, int h_kv, in
  *   out            device [batch, s_q, h_q, 512] of dtype, 16-byte aligned,
  *                  rounded to nearest even
  *   lse            device fp32 [batch, s_q, h_q], natural log
- *   workspace      device, >= mla_decode_workspace_size(batch, M, h_kv,
- *                  num_parts) bytes, 16-byte aligned; contents are scratch
+ *   workspace      device, >= mla_workspace_bytes(batch, M, h_kv, num_parts,
+ *                  512) bytes, 16-byte aligned; contents are scratch
  * Enqueues the main kernel and, when a sequence has several pieces, the
  * combine kernel.  Concurrent calls must use distinct workspaces.
  */
@@ -184,36 +208,6 @@ int mla_decode_splitkv(const void *q, const void *blocked_k, const int32_t *bloc
 int mla_decode_combine(const int32_t *num_splits, int batch, int s_q, int h_q, int h_kv,
                        int num_parts, int dtype, void *out, float *lse, const void *workspace,
                        size_t workspace_bytes, void *stream);
-
-/* ---- Measurement helpers (not part of the decode path) --------------------
- * Ceilings measured on the running machine, against which the main kernel's
- * throughput is quoted besides the datasheet peaks.  They compute nothing of
- * the method; the benchmark is their only caller.
- *
- * mla_ceiling_stream: each of num_workgroups workgroups streams the
- * pages_per_workgroup cache pages listed in
- * pages[w * pages_per_workgroup + i] through a 4-slot LDS ring of
- * 36,864-byte stages with 16-byte LDS-DMA loads, two stages ahead, as the main
- * kernel's 16-row tile does; no arithmetic.
- *   pool        device, num_pages pages of page_bytes bytes (one KV head)
- *   page_bytes  must be 73,728 (64 rows x 1152 B); num_pages * page_bytes
- *               must be below 2^31; a page index outside the pool loads
- *               zeros (no fault)
- *   pages       device int32 [num_workgroups, pages_per_workgroup]
- *   sink        device int32 [1]; written only in a case that does not occur
- *               for real data (it keeps the loads from being optimised away)
- * Bytes read = num_workgroups * pages_per_workgroup * page_bytes.
- *
- * mla_ceiling_mfma: num_workgroups workgroups of 4 waves; each wave runs
- * iters x 4 independent 32x32x16 bf16 MFMAs (32768 flops each).
- *   sink   device float [1], same role as above
- * Flops = num_workgroups * 4 * iters * 4 * 32768.
- * Both return MLA_ERR_INVALID_ARG for null pointers or sizes outside the
- * stated ranges and enqueue on `stream`.
- */
-int mla_ceiling_stream(const void *pool, int num_pages, int page_bytes, const int32_t *pages,
-                       int num_workgroups, int pages_per_workgroup, int32_t *sink, void *stream);
-int mla_ceiling_mfma(float *sink, int num_workgroups, int iters, void *stream);
 
 #ifdef __cplusplus
 }

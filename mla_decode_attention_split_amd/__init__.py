@@ -4,9 +4,10 @@ Thin binding over ``libmla_decode.so`` (C ABI in ``include/mla_decode.h``):
 argument marshalling only -- every step of the decode runs in the library's
 HIP kernels.  PyTorch provides device memory and the current stream.
 
-Entry points with the C names: :func:`mla_get_metadata_shape`,
-:func:`mla_get_metadata`, :func:`mla_decode_workspace_size`,
-:func:`mla_decode`.  The two calls the pages show ("DeepSeek 开源记-第1天-
+Entry points with the C names: :func:`mla_metadata_shape`,
+:func:`mla_tile_shape`, :func:`mla_get_metadata` (the C calls
+``mla_get_metadata`` / ``mla_get_metadata_ex``), :func:`mla_workspace_bytes`,
+:func:`mla_decode`, :func:`mla_decode_splitkv`, :func:`mla_decode_combine`.  The two calls the pages show ("DeepSeek 开源记-第1天-
 FlashMLA", section 6) are :func:`get_mla_metadata` and
 :func:`flash_mla_with_kvcache`, with the same argument order.
 
@@ -17,10 +18,11 @@ from __future__ import annotations
 
 import ctypes
 import os
+import sys
 
 __all__ = [
-    "MlaError", "library_path", "mla_get_metadata_shape", "mla_get_metadata",
-    "mla_decode_workspace_size", "mla_decode", "mla_decode_splitkv", "mla_decode_combine",
+    "MlaError", "library_path", "mla_metadata_shape", "mla_tile_shape", "mla_get_metadata",
+    "mla_workspace_bytes", "mla_decode", "mla_decode_splitkv", "mla_decode_combine",
     "get_mla_metadata", "flash_mla_with_kvcache",
     "HEAD_DIM", "VALUE_DIM", "PAGE_SIZE",
 ]
@@ -61,13 +63,17 @@ def _load():
     lib.mla_status_string.restype = ctypes.c_char_p
     lib.mla_last_error.argtypes = []
     lib.mla_last_error.restype = ctypes.c_char_p
-    lib.mla_get_metadata_shape.argtypes = [i, i, i, ctypes.POINTER(i), ctypes.POINTER(i),
-                                           ctypes.POINTER(i)]
-    lib.mla_get_metadata_shape.restype = i
-    lib.mla_get_metadata.argtypes = [p, i, i, i, i, i, p, p, p]
+    pi = ctypes.POINTER(i)
+    lib.mla_metadata_shape.argtypes = [i, i, i, pi, pi]
+    lib.mla_metadata_shape.restype = i
+    lib.mla_tile_shape.argtypes = [i, i, pi, pi, pi]
+    lib.mla_tile_shape.restype = i
+    lib.mla_get_metadata.argtypes = [p, i, i, i, p, p, p]
     lib.mla_get_metadata.restype = i
-    lib.mla_decode_workspace_size.argtypes = [i, i, i, i]
-    lib.mla_decode_workspace_size.restype = sz
+    lib.mla_get_metadata_ex.argtypes = [p, i, i, i, p, p, p, i, i]
+    lib.mla_get_metadata_ex.restype = i
+    lib.mla_workspace_bytes.argtypes = [i, i, i, i, i]
+    lib.mla_workspace_bytes.restype = sz
     decode_args = [p, p, p, p, i, i, i, i, i, i, i, i, i, i, p, i, p, i, ctypes.c_float, p, p, p,
                    sz, p]
     lib.mla_decode.argtypes = decode_args
@@ -76,10 +82,6 @@ def _load():
     lib.mla_decode_splitkv.restype = i
     lib.mla_decode_combine.argtypes = [p, i, i, i, i, i, i, p, p, p, sz, p]
     lib.mla_decode_combine.restype = i
-    lib.mla_ceiling_stream.argtypes = [p, i, i, p, i, i, p, p]
-    lib.mla_ceiling_stream.restype = i
-    lib.mla_ceiling_mfma.argtypes = [p, i, i, p]
-    lib.mla_ceiling_mfma.restype = i
     _lib = lib
     return lib
 
@@ -95,13 +97,25 @@ def _stream_of(device):
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
 
-def mla_get_metadata_shape(batch: int, q_rows_per_kv_head: int, h_kv: int):
-    """Returns ``(num_parts, fixed_cost, tile_rows)`` for the current device."""
+def mla_metadata_shape(batch: int, q_rows_per_kv_head: int, h_kv: int):
+    """Returns ``(num_parts, words_per_part)`` of the default partition on the
+    current device: ``tile_metadata`` is int32 ``[num_parts, words_per_part]``."""
     lib = _load()
-    n, f, t = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
-    _check(lib.mla_get_metadata_shape(int(batch), int(q_rows_per_kv_head), int(h_kv),
-                                      ctypes.byref(n), ctypes.byref(f), ctypes.byref(t)))
-    return n.value, f.value, t.value
+    n, wpp = ctypes.c_int(), ctypes.c_int()
+    _check(lib.mla_metadata_shape(int(batch), int(q_rows_per_kv_head), int(h_kv), ctypes.byref(n),
+                                  ctypes.byref(wpp)))
+    return n.value, wpp.value
+
+
+def mla_tile_shape(q_rows_per_kv_head: int, h_kv: int):
+    """Returns ``(tile_rows, m_tiles, fixed_cost)``: the decode kernel's row tile
+    for this many rows per KV head and the partition's default per-sequence
+    cost (32-key units)."""
+    lib = _load()
+    t, m, f = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
+    _check(lib.mla_tile_shape(int(q_rows_per_kv_head), int(h_kv), ctypes.byref(t), ctypes.byref(m),
+                              ctypes.byref(f)))
+    return t.value, m.value, f.value
 
 
 def mla_get_metadata(cache_seqlens, q_rows_per_kv_head: int, h_kv: int, *,
@@ -109,8 +123,9 @@ def mla_get_metadata(cache_seqlens, q_rows_per_kv_head: int, h_kv: int, *,
                      tile_metadata=None, num_splits=None):
     """Split-KV scheduling metadata on the device of ``cache_seqlens``.
 
-    Returns ``(tile_metadata int32 [num_parts, 8], num_splits int32 [B+1])``;
-    ``num_parts`` / ``fixed_cost`` default to :func:`mla_get_metadata_shape`.
+    Returns ``(tile_metadata int32 [num_parts, 8], num_splits int32 [B+1])``.
+    ``num_parts`` / ``fixed_cost`` override the library's defaults (the C call
+    ``mla_get_metadata_ex``); without them this is ``mla_get_metadata``.
     Preallocated output tensors may be passed in.
     """
     import torch
@@ -119,15 +134,12 @@ def mla_get_metadata(cache_seqlens, q_rows_per_kv_head: int, h_kv: int, *,
     seqlens = cache_seqlens.contiguous()
     batch = seqlens.shape[0]
     with torch.cuda.device(seqlens.device):
-        if num_parts is None or fixed_cost is None:
-            dn, df, _ = mla_get_metadata_shape(batch, q_rows_per_kv_head, h_kv)
-            num_parts = dn if num_parts is None else int(num_parts)
-            fixed_cost = df if fixed_cost is None else int(fixed_cost)
+        parts = int(num_parts) if num_parts is not None else \
+            mla_metadata_shape(batch, q_rows_per_kv_head, h_kv)[0]
         meta = tile_metadata
         if meta is None:
-            meta = torch.empty((num_parts, METADATA_WORDS), dtype=torch.int32,
-                               device=seqlens.device)
-        elif (meta.dtype != torch.int32 or tuple(meta.shape) != (num_parts, METADATA_WORDS)
+            meta = torch.empty((parts, METADATA_WORDS), dtype=torch.int32, device=seqlens.device)
+        elif (meta.dtype != torch.int32 or tuple(meta.shape) != (parts, METADATA_WORDS)
               or not meta.is_contiguous()):
             raise ValueError("tile_metadata must be contiguous int32 [num_parts, 8]")
         splits = num_splits
@@ -135,16 +147,29 @@ def mla_get_metadata(cache_seqlens, q_rows_per_kv_head: int, h_kv: int, *,
             splits = torch.empty((batch + 1,), dtype=torch.int32, device=seqlens.device)
         elif splits.dtype != torch.int32 or tuple(splits.shape) != (batch + 1,):
             raise ValueError("num_splits must be int32 [B+1]")
-        _check(_load().mla_get_metadata(seqlens.data_ptr(), batch, int(q_rows_per_kv_head),
-                                        int(h_kv), num_parts, fixed_cost, meta.data_ptr(),
-                                        splits.data_ptr(), _stream_of(seqlens.device)))
+        lib = _load()
+        stream = _stream_of(seqlens.device)
+        if num_parts is None and fixed_cost is None:
+            _check(lib.mla_get_metadata(seqlens.data_ptr(), batch, int(q_rows_per_kv_head),
+                                        int(h_kv), meta.data_ptr(), splits.data_ptr(), stream))
+        else:
+            _check(lib.mla_get_metadata_ex(seqlens.data_ptr(), batch, int(q_rows_per_kv_head),
+                                           int(h_kv), meta.data_ptr(), splits.data_ptr(), stream,
+                                           parts if num_parts is not None else 0,
+                                           int(fixed_cost) if fixed_cost is not None else 0))
+        if os.environ.get("MLA_DECODE_LOG", "0") not in ("", "0"):
+            # debugging aid only: this reads num_splits back (a device sync)
+            pieces = (splits[1:] - splits[:-1]).cpu()
+            print(f"[mla] split stats: {int(pieces.sum())} pieces over {batch} sequences, "
+                  f"max {int(pieces.max())}, split sequences {int((pieces > 1).sum())}",
+                  file=sys.stderr, flush=True)
     return meta, splits
 
 
-def mla_decode_workspace_size(batch: int, q_rows_per_kv_head: int, h_kv: int,
-                              num_parts: int) -> int:
-    return int(_load().mla_decode_workspace_size(int(batch), int(q_rows_per_kv_head), int(h_kv),
-                                                 int(num_parts)))
+def mla_workspace_bytes(batch: int, q_rows_per_kv_head: int, h_kv: int, num_parts: int,
+                        dv: int = VALUE_DIM) -> int:
+    return int(_load().mla_workspace_bytes(int(batch), int(q_rows_per_kv_head), int(h_kv),
+                                           int(num_parts), int(dv)))
 
 
 def _decode_call(fn_name, q, blocked_k, block_table, cache_seqlens, tile_metadata, num_splits,
@@ -186,7 +211,7 @@ def _decode_call(fn_name, q, blocked_k, block_table, cache_seqlens, tile_metadat
             raise ValueError("out must have q's dtype")
         if lse is None:
             lse = torch.empty((B, s_q, h_q), dtype=torch.float32, device=dev)
-        need = mla_decode_workspace_size(B, M, h_kv, num_parts) if h_q % max(h_kv, 1) == 0 else 0
+        need = mla_workspace_bytes(B, M, h_kv, num_parts) if h_q % max(h_kv, 1) == 0 else 0
         if workspace is None:
             workspace = torch.empty((max(need, 16),), dtype=torch.uint8, device=dev)
         fn = getattr(_load(), fn_name)
@@ -233,35 +258,15 @@ def mla_decode_combine(num_splits, out, lse, workspace, *, num_parts: int, h_kv:
     return out, lse
 
 
-def mla_ceiling_stream(pool, pages, sink):
-    """Measurement helper: stream the cache pages listed in ``pages`` (int32
-    ``[workgroups, pages_per_workgroup]``) of ``pool`` (bf16
-    ``[num_pages, 64, 1, 576]``) through the main kernel's LDS ring, no
-    arithmetic.  ``sink`` is an int32 device tensor of one element."""
-    W, P = pages.shape
-    with _torch_device(pool.device):
-        _check(_load().mla_ceiling_stream(
-            pool.data_ptr(), int(pool.shape[0]), pool[0].numel() * pool.element_size(),
-            pages.data_ptr(), int(W), int(P), sink.data_ptr(), _stream_of(pool.device)))
-
-
-def mla_ceiling_mfma(sink, num_workgroups: int, iters: int):
-    """Measurement helper: ``num_workgroups`` x 4 waves of ``iters`` x 4
-    independent 32x32x16 bf16 MFMAs.  ``sink`` is a float device tensor of
-    one element."""
-    with _torch_device(sink.device):
-        _check(_load().mla_ceiling_mfma(sink.data_ptr(), int(num_workgroups), int(iters),
-                                        _stream_of(sink.device)))
-
-
 def _torch_device(dev):
     import torch
     return torch.cuda.device(dev)
 
 
 def get_mla_metadata(cache_seqlens, num_heads_per_head_k: int, num_heads_k: int):
-    """The pages' metadata call: ``get_mla_metadata(cache_seqlens,
-    s_q * h_q // h_kv, h_kv)`` -> ``(tile_scheduler_metadata, num_splits)``."""
+    """The pages' metadata call (cnblogs page, section 6): the cache lengths,
+    the query rows per KV head and the KV head count in; the scheduling
+    metadata and the per-sequence split counts out."""
     return mla_get_metadata(cache_seqlens, num_heads_per_head_k, num_heads_k)
 
 

@@ -1,8 +1,13 @@
-"""Build libmla_decode.so in-tree with hipcc for gfx950.
+"""Build the HIP libraries in-tree with hipcc for gfx950.
 
 Usage: ``python -m mla_decode_attention_split_amd.build`` (or call
 :func:`build`).  Every HIP source is compiled with packed-fp32 instructions
-disabled and linked into one shared library next to this file.
+disabled.  Two shared libraries are linked next to this file:
+
+* ``libmla_decode.so`` -- the decode path (C ABI in include/mla_decode.h);
+* ``libmla_ceiling.so`` -- the measurement probes the benchmark quotes the
+  decode kernel against (C ABI in include/mla_ceiling.h); not linked by the
+  decode library.
 """
 from __future__ import annotations
 
@@ -14,7 +19,9 @@ from concurrent.futures import ThreadPoolExecutor
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmla_decode.so")
-SOURCES = ["api.hip", "sched.hip", "decode.hip", "combine.hip", "ceiling.hip"]
+CEILING_LIB = os.path.join(HERE, "libmla_ceiling.so")
+SOURCES = ["api.hip", "sched.hip", "decode.hip", "combine.hip"]
+CEILING_SOURCES = ["ceiling.hip"]
 ARCH = os.environ.get("MLA_OFFLOAD_ARCH", "gfx950")
 
 COMMON = [
@@ -41,22 +48,28 @@ def _run(cmd):
         print(err, file=sys.stderr)
 
 
+def _link(objs, lib):
+    tmp = lib + ".tmp"
+    _run(["hipcc", "--offload-arch=" + ARCH, "-shared", "-fPIC", *objs, "-o", tmp])
+    os.replace(tmp, lib)
+
+
 def build(verbose: bool = False) -> str:
     objdir = os.path.join(HERE, "_build")
     os.makedirs(objdir, exist_ok=True)
-    objs = []
     cmds = []
-    for s in SOURCES:
-        obj = os.path.join(objdir, s.replace(".hip", ".o"))
-        objs.append(obj)
-        cmds.append(["hipcc", *COMMON, *EXTRA.get(s, []), "-c", os.path.join(CSRC, s), "-o", obj])
+
+    def obj_of(s):
+        return os.path.join(objdir, s.replace(".hip", ".o"))
+
+    for s in SOURCES + CEILING_SOURCES:
+        cmds.append(["hipcc", *COMMON, *EXTRA.get(s, []), "-c", os.path.join(CSRC, s), "-o", obj_of(s)])
     with ThreadPoolExecutor(max_workers=min(4, os.cpu_count() or 1)) as ex:
         list(ex.map(_run, cmds))
-    tmp = LIB + ".tmp"
-    _run(["hipcc", "--offload-arch=" + ARCH, "-shared", "-fPIC", *objs, "-o", tmp])
-    os.replace(tmp, LIB)
+    _link([obj_of(s) for s in SOURCES], LIB)
+    _link([obj_of(s) for s in CEILING_SOURCES], CEILING_LIB)
     if verbose:
-        print("built", LIB)
+        print("built", LIB, "and", CEILING_LIB)
     return LIB
 
 

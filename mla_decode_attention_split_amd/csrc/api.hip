@@ -5,6 +5,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <mutex>
 
 #include "../../include/mla_decode.h"
@@ -50,6 +51,17 @@ int device_cus(int* cus) {
   return MLA_OK;
 }
 
+// MLA_DECODE_LOG=1 in the environment: every metadata and decode call prints
+// its launch configuration to stderr (read once per process; no effect on
+// the results).
+bool log_enabled() {
+  static const bool on = [] {
+    const char* v = std::getenv("MLA_DECODE_LOG");
+    return v && v[0] && !(v[0] == '0' && v[1] == '\0');
+  }();
+  return on;
+}
+
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 int check_rows(int q_rows_per_kv_head, int h_kv) {
@@ -77,52 +89,94 @@ const char* mla_status_string(int status) {
 
 const char* mla_last_error(void) { return g_err; }
 
-int mla_get_metadata_shape(int batch, int q_rows_per_kv_head, int h_kv, int* num_parts,
-                           int* fixed_cost, int* tile_rows) {
-  if (batch < 1 || batch > MLA_MAX_BATCH)
-    return fail(MLA_ERR_INVALID_ARG, "batch %d outside [1, %d]", batch, MLA_MAX_BATCH);
+namespace {
+
+// Default partition parameters for M rows per KV head on the current device.
+int default_partition(int q_rows_per_kv_head, int h_kv, int* num_parts, int* fixed_cost,
+                      int* tile_rows, int* m_tiles) {
   int rc = check_rows(q_rows_per_kv_head, h_kv);
   if (rc != MLA_OK) return rc;
-  int cus = 0;
-  rc = device_cus(&cus);
-  if (rc != MLA_OK) return rc;
   const int tr = mla::tile_rows_for(q_rows_per_kv_head);
-  const int m_tiles = (q_rows_per_kv_head + tr - 1) / tr;
-  // One workgroup per compute unit: parts x row tiles x KV heads ~ CUs,
-  // rounded down to a multiple of 8 so each part's tiles share an XCD.
-  int parts = cus / (m_tiles * h_kv);
-  parts = parts >= 8 ? (parts / 8) * 8 : 8;
-  if (num_parts) *num_parts = parts;
+  const int mt = (q_rows_per_kv_head + tr - 1) / tr;
+  if (num_parts) {
+    int cus = 0;
+    rc = device_cus(&cus);
+    if (rc != MLA_OK) return rc;
+    // One workgroup per compute unit: parts x row tiles x KV heads ~ CUs,
+    // rounded down to a multiple of 8 so each part's tiles share an XCD.
+    int parts = cus / (mt * h_kv);
+    parts = parts >= 8 ? (parts / 8) * 8 : 8;
+    *num_parts = parts;
+  }
   // Per-sequence overhead in 32-key stage units: the query stages of a piece
   // (one per 32 query rows of the tile) plus about one stage for the
   // epilogue and the merge of one more piece.
   if (fixed_cost) *fixed_cost = (tr + 31) / 32 + 1;
   if (tile_rows) *tile_rows = tr;
+  if (m_tiles) *m_tiles = mt;
+  return MLA_OK;
+}
+
+}  // namespace
+
+int mla_metadata_shape(int batch, int q_rows_per_kv_head, int h_kv, int* num_parts,
+                       int* words_per_part) {
+  if (batch < 1 || batch > MLA_MAX_BATCH)
+    return fail(MLA_ERR_INVALID_ARG, "batch %d outside [1, %d]", batch, MLA_MAX_BATCH);
+  int parts = 0;
+  int rc = default_partition(q_rows_per_kv_head, h_kv, &parts, nullptr, nullptr, nullptr);
+  if (rc != MLA_OK) return rc;
+  if (num_parts) *num_parts = parts;
+  if (words_per_part) *words_per_part = MLA_METADATA_WORDS;
   return ok();
 }
 
-int mla_get_metadata(const int32_t* cache_seqlens, int batch, int q_rows_per_kv_head, int h_kv,
-                     int num_parts, int fixed_cost, int32_t* tile_metadata, int32_t* num_splits,
-                     void* stream) {
+int mla_tile_shape(int q_rows_per_kv_head, int h_kv, int* tile_rows, int* m_tiles, int* fixed_cost) {
+  int rc = default_partition(q_rows_per_kv_head, h_kv, nullptr, fixed_cost, tile_rows, m_tiles);
+  if (rc != MLA_OK) return rc;
+  return ok();
+}
+
+int mla_get_metadata_ex(const int32_t* cache_seqlens, int batch, int q_rows_per_kv_head, int h_kv,
+                        int32_t* tile_metadata, int32_t* num_splits, void* stream,
+                        int num_parts_override, int fixed_cost_override) {
   if (batch < 1 || batch > MLA_MAX_BATCH)
     return fail(MLA_ERR_INVALID_ARG, "batch %d outside [1, %d]", batch, MLA_MAX_BATCH);
-  int rc = check_rows(q_rows_per_kv_head, h_kv);
-  if (rc != MLA_OK) return rc;
-  if (num_parts < 1 || num_parts > MLA_MAX_PARTS)
-    return fail(MLA_ERR_INVALID_ARG, "num_parts %d outside [1, %d]", num_parts, MLA_MAX_PARTS);
-  if (fixed_cost < 1) return fail(MLA_ERR_INVALID_ARG, "fixed_cost %d < 1", fixed_cost);
+  if (num_parts_override < 0 || num_parts_override > MLA_MAX_PARTS)
+    return fail(MLA_ERR_INVALID_ARG, "num_parts_override %d outside [0, %d]", num_parts_override,
+                MLA_MAX_PARTS);
+  if (fixed_cost_override < 0)
+    return fail(MLA_ERR_INVALID_ARG, "fixed_cost_override %d < 0", fixed_cost_override);
   if (!cache_seqlens || !tile_metadata || !num_splits)
     return fail(MLA_ERR_INVALID_ARG, "null pointer (cache_seqlens, tile_metadata, num_splits)");
   if (!aligned16(tile_metadata)) return fail(MLA_ERR_INVALID_ARG, "tile_metadata not 16-byte aligned");
+  int num_parts = 0, fixed_cost = 0;
+  int rc = default_partition(q_rows_per_kv_head, h_kv, num_parts_override ? nullptr : &num_parts,
+                             &fixed_cost, nullptr, nullptr);
+  if (rc != MLA_OK) return rc;
+  if (num_parts_override) num_parts = num_parts_override;
+  if (fixed_cost_override) fixed_cost = fixed_cost_override;
+  if (log_enabled())
+    std::fprintf(stderr, "[mla] get_metadata: batch %d rows/kv-head %d h_kv %d -> num_parts %d%s, "
+                 "fixed_cost %d%s\n", batch, q_rows_per_kv_head, h_kv, num_parts,
+                 num_parts_override ? " (override)" : "", fixed_cost,
+                 fixed_cost_override ? " (override)" : "");
   hipError_t e = mla::launch_sched(cache_seqlens, batch, num_parts, fixed_cost, tile_metadata,
                                    num_splits, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(MLA_ERR_HIP, "scheduler launch: %s", hipGetErrorString(e));
   return ok();
 }
 
-size_t mla_decode_workspace_size(int batch, int q_rows_per_kv_head, int h_kv, int num_parts) {
+int mla_get_metadata(const int32_t* cache_seqlens, int batch, int q_rows_per_kv_head, int h_kv,
+                     int32_t* tile_metadata, int32_t* num_splits, void* stream) {
+  return mla_get_metadata_ex(cache_seqlens, batch, q_rows_per_kv_head, h_kv, tile_metadata,
+                             num_splits, stream, 0, 0);
+}
+
+size_t mla_workspace_bytes(int batch, int q_rows_per_kv_head, int h_kv, int num_parts, int dv) {
   if (batch < 1 || batch > MLA_MAX_BATCH || q_rows_per_kv_head < 1 ||
-      q_rows_per_kv_head > MLA_MAX_ROWS || h_kv < 1 || num_parts < 1 || num_parts > MLA_MAX_PARTS)
+      q_rows_per_kv_head > MLA_MAX_ROWS || h_kv < 1 || num_parts < 1 || num_parts > MLA_MAX_PARTS ||
+      dv != MLA_VALUE_DIM)
     return 0;
   const size_t pieces = (size_t)batch + (size_t)num_parts;
   const size_t rows = pieces * (size_t)h_kv * (size_t)q_rows_per_kv_head;
@@ -176,7 +230,7 @@ int prepare_decode(const void* q, const void* blocked_k, const int32_t* block_ta
     return fail(MLA_ERR_INVALID_ARG, "null pointer argument");
   if (!aligned16(q) || !aligned16(blocked_k) || !aligned16(out) || !aligned16(workspace))
     return fail(MLA_ERR_INVALID_ARG, "q, blocked_k, out and workspace must be 16-byte aligned");
-  const size_t need = mla_decode_workspace_size(batch, M, h_kv, num_parts);
+  const size_t need = mla_workspace_bytes(batch, M, h_kv, num_parts, MLA_VALUE_DIM);
   if (workspace_bytes < need)
     return fail(MLA_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", workspace_bytes, need);
 
@@ -209,6 +263,11 @@ int prepare_decode(const void* q, const void* blocked_k, const int32_t* block_ta
   const long long grid = (long long)num_parts * a->m_tiles * h_kv;
   if (grid > 0x7fffffffLL) return fail(MLA_ERR_UNSUPPORTED, "grid too large");
   *tile_rows = tr;
+  if (log_enabled())
+    std::fprintf(stderr, "[mla] decode: batch %d s_q %d h_q %d h_kv %d rows/kv-head %d %s causal %d "
+                 "-> tile_rows %d m_tiles %d num_parts %d grid %lld (xcd map %d)\n", batch, s_q, h_q,
+                 h_kv, M, a->f16 ? "fp16" : "bf16", a->causal, tr, a->m_tiles, num_parts, grid,
+                 a->xcd_map);
   return MLA_OK;
 }
 
@@ -271,7 +330,7 @@ int mla_decode_combine(const int32_t* num_splits, int batch, int s_q, int h_q, i
   if (!aligned16(out) || !aligned16(workspace))
     return fail(MLA_ERR_INVALID_ARG, "out and workspace must be 16-byte aligned");
   const int M = (int)M_ll;
-  const size_t need = mla_decode_workspace_size(batch, M, h_kv, num_parts);
+  const size_t need = mla_workspace_bytes(batch, M, h_kv, num_parts, MLA_VALUE_DIM);
   if (workspace_bytes < need)
     return fail(MLA_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", workspace_bytes, need);
   const size_t rows = ((size_t)batch + (size_t)num_parts) * (size_t)h_kv * (size_t)M;
@@ -312,33 +371,6 @@ int mla_decode(const void* q, const void* blocked_k, const int32_t* block_table,
   if (e != hipSuccess) return fail(MLA_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
   rc = enqueue_combine(a, st);
   if (rc != MLA_OK) return rc;
-  return ok();
-}
-
-int mla_ceiling_stream(const void* pool, int num_pages, int page_bytes, const int32_t* pages,
-                       int num_workgroups, int pages_per_workgroup, int32_t* sink, void* stream) {
-  if (!pool || !pages || !sink) return fail(MLA_ERR_INVALID_ARG, "null pointer argument");
-  if (page_bytes != 2 * mla::kStageBytes)
-    return fail(MLA_ERR_INVALID_ARG, "page_bytes %d != %d", page_bytes, 2 * mla::kStageBytes);
-  if (num_pages < 1 || (long long)num_pages * page_bytes >= (1LL << 31))
-    return fail(MLA_ERR_INVALID_ARG, "num_pages %d outside [1, 2^31 / page_bytes)", num_pages);
-  if (num_workgroups < 1 || num_workgroups > (1 << 20) || pages_per_workgroup < 1 ||
-      pages_per_workgroup > (1 << 16))
-    return fail(MLA_ERR_INVALID_ARG, "num_workgroups %d, pages_per_workgroup %d", num_workgroups,
-                pages_per_workgroup);
-  hipError_t e = mla::launch_stream_ceiling(pool, (unsigned)((long long)num_pages * page_bytes), pages,
-                                            num_workgroups, pages_per_workgroup, sink,
-                                            static_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return fail(MLA_ERR_HIP, "stream ceiling launch: %s", hipGetErrorString(e));
-  return ok();
-}
-
-int mla_ceiling_mfma(float* sink, int num_workgroups, int iters, void* stream) {
-  if (!sink) return fail(MLA_ERR_INVALID_ARG, "null pointer argument");
-  if (num_workgroups < 1 || num_workgroups > (1 << 20) || iters < 1 || iters > (1 << 24))
-    return fail(MLA_ERR_INVALID_ARG, "num_workgroups %d, iters %d", num_workgroups, iters);
-  hipError_t e = mla::launch_mfma_ceiling(sink, num_workgroups, iters, static_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return fail(MLA_ERR_HIP, "mfma ceiling launch: %s", hipGetErrorString(e));
   return ok();
 }
 

@@ -1,6 +1,7 @@
-// Measurement kernels: the ceilings that the main kernel is quoted against on
-// the machine it runs on.  They are not part of the decode path and compute
-// nothing of the method.
+// libmla_ceiling.so: measurement kernels, the ceilings that the main kernel is
+// quoted against on the machine it runs on.  They are not part of the decode
+// path, compute nothing of the method, and are built into their own library
+// (C ABI in include/mla_ceiling.h).
 //
 //   * stream_ceiling_kernel: every workgroup streams a list of cache pages
 //     (64 rows x 1152 B, one KV head) through a 4-slot LDS ring of
@@ -11,8 +12,11 @@
 //   * mfma_ceiling_kernel: every wave runs four independent chains of
 //     32x32x16 bf16 MFMAs: the dense bf16 MFMA rate at the clock the chip
 //     holds under that load.
+#include <cstdarg>
+#include <cstdio>
+
+#include "../../include/mla_ceiling.h"
 #include "mla_common.hpp"
-#include "mla_internal.hpp"
 
 namespace mla {
 
@@ -83,16 +87,58 @@ __global__ __launch_bounds__(64 * kCeilWaves) void mfma_ceiling_kernel(float* __
   if (s == -1.0f) sink[0] = s;  // keeps the chains; never true for these inputs
 }
 
-hipError_t launch_stream_ceiling(const void* pool, unsigned pool_bytes, const int32_t* pages,
-                                 int num_wg, int pages_per_wg, int* sink, hipStream_t stream) {
-  hipLaunchKernelGGL(stream_ceiling_kernel, dim3(num_wg), dim3(64 * kCeilWaves), 0, stream,
-                     static_cast<const char*>(pool), pool_bytes, pages, pages_per_wg, sink);
-  return hipGetLastError();
-}
-
-hipError_t launch_mfma_ceiling(float* sink, int num_wg, int iters, hipStream_t stream) {
-  hipLaunchKernelGGL(mfma_ceiling_kernel, dim3(num_wg), dim3(64 * kCeilWaves), 0, stream, sink, iters);
-  return hipGetLastError();
-}
-
 }  // namespace mla
+
+namespace {
+
+thread_local char g_err[256] = "";
+
+int fail(int status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+constexpr int kOk = 0, kInvalid = -1, kHip = -4;
+
+}  // namespace
+
+extern "C" {
+
+const char* mla_ceiling_last_error(void) { return g_err; }
+
+int mla_ceiling_stream(const void* pool, int num_pages, int page_bytes, const int32_t* pages,
+                       int num_workgroups, int pages_per_workgroup, int32_t* sink, void* stream) {
+  if (!pool || !pages || !sink) return fail(kInvalid, "null pointer argument");
+  if (page_bytes != 2 * mla::kStageBytes)
+    return fail(kInvalid, "page_bytes %d != %d", page_bytes, 2 * mla::kStageBytes);
+  if (num_pages < 1 || (long long)num_pages * page_bytes >= (1LL << 31))
+    return fail(kInvalid, "num_pages %d outside [1, 2^31 / page_bytes)", num_pages);
+  if (num_workgroups < 1 || num_workgroups > (1 << 20) || pages_per_workgroup < 1 ||
+      pages_per_workgroup > (1 << 16))
+    return fail(kInvalid, "num_workgroups %d, pages_per_workgroup %d", num_workgroups,
+                pages_per_workgroup);
+  hipLaunchKernelGGL(mla::stream_ceiling_kernel, dim3(num_workgroups), dim3(64 * mla::kCeilWaves), 0,
+                     static_cast<hipStream_t>(stream), static_cast<const char*>(pool),
+                     (unsigned)((long long)num_pages * page_bytes), pages, pages_per_workgroup, sink);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(kHip, "stream ceiling launch: %s", hipGetErrorString(e));
+  g_err[0] = '\0';
+  return kOk;
+}
+
+int mla_ceiling_mfma(float* sink, int num_workgroups, int iters, void* stream) {
+  if (!sink) return fail(kInvalid, "null pointer argument");
+  if (num_workgroups < 1 || num_workgroups > (1 << 20) || iters < 1 || iters > (1 << 24))
+    return fail(kInvalid, "num_workgroups %d, iters %d", num_workgroups, iters);
+  hipLaunchKernelGGL(mla::mfma_ceiling_kernel, dim3(num_workgroups), dim3(64 * mla::kCeilWaves), 0,
+                     static_cast<hipStream_t>(stream), sink, iters);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(kHip, "mfma ceiling launch: %s", hipGetErrorString(e));
+  g_err[0] = '\0';
+  return kOk;
+}
+
+}  // extern "C"

@@ -45,8 +45,5 @@ hipError_t launch_sched(const int32_t* seqlens, int batch, int num_parts, int fi
                         int32_t* meta, int32_t* num_splits, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, int tile_rows, hipStream_t stream);
 hipError_t launch_combine(CombineArgs a, int num_parts, hipStream_t stream);
-hipError_t launch_stream_ceiling(const void* pool, unsigned pool_bytes, const int32_t* pages,
-                                 int num_wg, int pages_per_wg, int* sink, hipStream_t stream);
-hipError_t launch_mfma_ceiling(float* sink, int num_wg, int iters, hipStream_t stream);
 
 }  // namespace mla

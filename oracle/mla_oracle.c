@@ -20,8 +20,9 @@
  *     tile_scheduler_metadata, num_splits, causal) and the (output, lse) pair.
  *   - "DeepSeek代碼開源第一彈Flash MLA" (ygpos news): BF16, paged KV cache with
  *     block size 64, variable-length sequences.
- *   - "什么是FlashMLA" (jsxs2.com), section on supported precisions: FP16
- *     beside BF16.
+ *   - "DeepSeek 开源记-第1天-FlashMLA" (cnblogs), section 2 "核心功能": FP16
+ *     beside BF16 (the other pages name BF16 only; the jsxs2 explainer's
+ *     section 2.1 says BF16 only).
  *   - FlashMLA explainer (jsxs2.com), section 3.1 "分块调度与并行计算": the work
  *     is cut into small blocks that run in parallel (the split scheduler).
  *
@@ -308,10 +309,12 @@ int mla_oracle_decode_split(const uint16_t *q, const uint16_t *kcache, const int
  *   4. A piece is the run of one sequence's units inside one part; pieces of
  *      a sequence sit in consecutive parts.  num_splits[b+1] - num_splits[b]
  *      is the number of pieces of sequence b (num_splits[0] = 0).
- *   5. Per part p, 8 int32 words: first sequence, first key of its piece,
- *      last sequence, end key (exclusive, at most N) of its piece, the split
- *      index of the first sequence's piece, then three zero words.  A part
- *      with no piece stores first = 0, last = -1.
+ *   5. Per part p, 8 int32 words: first sequence bb, first key of its
+ *      piece, last sequence be, end key (exclusive, at most N) of its piece,
+ *      the partial slot of bb's piece (num_splits[bb] + its split index),
+ *      N_bb, N_be, and num_splits[be] (the partial slot of be's piece, whose
+ *      split index is 0).  A part with no piece stores first = 0, last = -1
+ *      and zeros elsewhere.
  */
 int mla_oracle_schedule(const int32_t *seqlens, int B, int unit_tokens, int num_parts,
                         int fixed_cost, int32_t *tile_meta, int32_t *num_splits) {

@@ -4,6 +4,7 @@ status codes before anything reaches the device."""
 import ctypes
 import os
 import re
+import subprocess
 
 import pytest
 
@@ -11,10 +12,20 @@ import mla_decode_attention_split_amd as mla
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "mla_decode.h")
+CEILING_HEADER = os.path.join(ROOT, "include", "mla_ceiling.h")
+CEILING_LIB = os.path.join(os.path.dirname(mla.library_path()), "libmla_ceiling.so")
+
+# The documented entry points of each library: the boundary's two calls, their
+# sizing helpers and override hook, the split halves of the decode, and the
+# status helpers.
+DECODE_API = {"mla_status_string", "mla_last_error", "mla_metadata_shape", "mla_tile_shape",
+              "mla_get_metadata", "mla_get_metadata_ex", "mla_workspace_bytes", "mla_decode",
+              "mla_decode_splitkv", "mla_decode_combine"}
+CEILING_API = {"mla_ceiling_stream", "mla_ceiling_mfma", "mla_ceiling_last_error"}
 
 
-def header_functions():
-    text = open(HEADER).read()
+def header_functions(path=HEADER):
+    text = open(path).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(mla_[a-z_]+)\s*\(", text)))
 
@@ -24,17 +35,30 @@ def header_constants():
                                                    open(HEADER).read()))
 
 
-def test_header_declares_the_two_calls_and_helpers():
-    names = header_functions()
-    for n in ("mla_get_metadata", "mla_decode", "mla_get_metadata_shape",
-              "mla_decode_workspace_size", "mla_status_string", "mla_last_error"):
-        assert n in names
+def exported_symbols(lib_path):
+    """Names of the global functions a shared library defines (nm -D)."""
+    out = subprocess.run(["nm", "-D", "--defined-only", lib_path], capture_output=True, text=True,
+                         check=True).stdout
+    return {ln.split()[-1] for ln in out.splitlines() if len(ln.split()) == 3 and ln.split()[1] == "T"}
 
 
-def test_library_exports_every_declared_symbol():
+def test_headers_declare_the_documented_api():
+    assert set(header_functions(HEADER)) == DECODE_API
+    assert set(header_functions(CEILING_HEADER)) == CEILING_API
+
+
+def test_library_exports_exactly_the_declared_symbols():
+    exported = {n for n in exported_symbols(mla.library_path()) if n.startswith("mla_")}
+    assert exported == DECODE_API, exported ^ DECODE_API
     lib = ctypes.CDLL(mla.library_path())
-    for name in header_functions():
+    for name in header_functions(HEADER):
         assert hasattr(lib, name), name
+
+
+def test_ceiling_library_is_separate():
+    exported = {n for n in exported_symbols(CEILING_LIB) if n.startswith("mla_")}
+    assert exported == CEILING_API, exported ^ CEILING_API
+    assert not (exported_symbols(mla.library_path()) & CEILING_API)
 
 
 def test_status_strings():
@@ -48,12 +72,27 @@ def test_status_strings():
 def test_workspace_size_formula():
     lib = mla._load()
     # (batch + num_parts) pieces x h_kv x rows x (512 fp32 + one fp32 lse, 256-B aligned)
-    n = lib.mla_decode_workspace_size(32, 16, 1, 256)
+    n = lib.mla_workspace_bytes(32, 16, 1, 256, 512)
     rows = (32 + 256) * 16
     assert n == rows * 512 * 4 + ((rows * 4 + 255) // 256) * 256
-    assert lib.mla_decode_workspace_size(0, 16, 1, 256) == 0
-    assert lib.mla_decode_workspace_size(4, 0, 1, 256) == 0
-    assert lib.mla_decode_workspace_size(4, 16, 1, 0) == 0
+    assert lib.mla_workspace_bytes(0, 16, 1, 256, 512) == 0
+    assert lib.mla_workspace_bytes(4, 0, 1, 256, 512) == 0
+    assert lib.mla_workspace_bytes(4, 16, 1, 0, 512) == 0
+    assert lib.mla_workspace_bytes(4, 16, 1, 256, 256) == 0
+
+
+def test_tile_shape_needs_no_device():
+    """mla_tile_shape is pure host arithmetic: 16/32/64-row tiles up to 64 rows
+    per KV head, 128-row tiles above; the default cost is the tile's query
+    stages plus one."""
+    for M, tr in [(1, 16), (16, 16), (17, 32), (32, 32), (33, 64), (64, 64), (65, 128), (256, 128),
+                  (4096, 128)]:
+        tile, m_tiles, fixed = mla.mla_tile_shape(M, 1)
+        assert (tile, m_tiles, fixed) == (tr, (M + tr - 1) // tr, (tr + 31) // 32 + 1)
+    with pytest.raises(mla.MlaError):
+        mla.mla_tile_shape(0, 1)
+    with pytest.raises(mla.MlaError):
+        mla.mla_tile_shape(4097, 1)
 
 
 FAKE = 1 << 20  # a 16-byte aligned non-null address; never dereferenced: every call below
@@ -101,13 +140,17 @@ def test_decode_rejects_bad_arguments(over, status):
 def test_metadata_rejects_bad_arguments():
     lib = mla._load()
     c = header_constants()
-    assert lib.mla_get_metadata(FAKE, 0, 16, 1, 8, 2, FAKE, FAKE, None) == c["MLA_ERR_INVALID_ARG"]
-    assert lib.mla_get_metadata(FAKE, 4, 16, 1, 0, 2, FAKE, FAKE, None) == c["MLA_ERR_INVALID_ARG"]
-    assert lib.mla_get_metadata(FAKE, 4, 16, 1, 8, 0, FAKE, FAKE, None) == c["MLA_ERR_INVALID_ARG"]
-    assert lib.mla_get_metadata(None, 4, 16, 1, 8, 2, FAKE, FAKE, None) == c["MLA_ERR_INVALID_ARG"]
-    assert lib.mla_get_metadata(FAKE, 4, 0, 1, 8, 2, FAKE, FAKE, None) == c["MLA_ERR_UNSUPPORTED"]
-    assert lib.mla_get_metadata(FAKE, 4, 16, 1, 8, 2, FAKE + 4, FAKE, None) == \
-        c["MLA_ERR_INVALID_ARG"]
+    bad, unsup = c["MLA_ERR_INVALID_ARG"], c["MLA_ERR_UNSUPPORTED"]
+    assert lib.mla_get_metadata(FAKE, 0, 16, 1, FAKE, FAKE, None) == bad
+    assert lib.mla_get_metadata(None, 4, 16, 1, FAKE, FAKE, None) == bad
+    assert lib.mla_get_metadata(FAKE, 4, 16, 1, None, FAKE, None) == bad
+    assert lib.mla_get_metadata(FAKE, 4, 0, 1, FAKE, FAKE, None) == unsup
+    assert lib.mla_get_metadata(FAKE, 4, 16, 1, FAKE + 4, FAKE, None) == bad
+    assert lib.mla_get_metadata_ex(FAKE, 4, 16, 1, FAKE, FAKE, None, -1, 0) == bad
+    assert lib.mla_get_metadata_ex(FAKE, 4, 16, 1, FAKE, FAKE, None, 65537, 0) == bad
+    assert lib.mla_get_metadata_ex(FAKE, 4, 16, 1, FAKE, FAKE, None, 8, -1) == bad
+    assert lib.mla_metadata_shape(0, 16, 1, None, None) == bad
+    assert lib.mla_metadata_shape(4, 4097, 1, None, None) == unsup
 
 
 def test_binding_rejects_wrong_value_dim():
@@ -116,10 +159,12 @@ def test_binding_rejects_wrong_value_dim():
 
 
 def test_ceiling_helpers_reject_bad_arguments():
-    """The measurement helpers check their arguments on the host (no GPU call)."""
-    lib = mla._load()
-    c = header_constants()
-    bad = c["MLA_ERR_INVALID_ARG"]
+    """The measurement probes check their arguments on the host (no GPU call)."""
+    lib = ctypes.CDLL(CEILING_LIB)
+    p, i = ctypes.c_void_p, ctypes.c_int
+    lib.mla_ceiling_stream.argtypes = [p, i, i, p, i, i, p, p]
+    lib.mla_ceiling_mfma.argtypes = [p, i, i, p]
+    bad = header_constants()["MLA_ERR_INVALID_ARG"]
     page = 64 * 1152
     assert lib.mla_ceiling_stream(None, 8, page, FAKE, 4, 2, FAKE, None) == bad
     assert lib.mla_ceiling_stream(FAKE, 8, page // 2, FAKE, 4, 2, FAKE, None) == bad
