@@ -20,7 +20,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmla_decode.so")
 CEILING_LIB = os.path.join(HERE, "libmla_ceiling.so")
-SOURCES = ["api.hip", "sched.hip", "decode.hip", "combine.hip"]
+SOURCES = ["api.hip", "sched.hip", "decode.hip", "decode_wide.hip", "combine.hip"]
 CEILING_SOURCES = ["ceiling.hip"]
 ARCH = os.environ.get("MLA_OFFLOAD_ARCH", "gfx950")
 
@@ -34,6 +34,7 @@ COMMON = [
 # multiply), which leaves the AGPRs free for operands the MFMAs read directly.
 EXTRA = {
     "decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    "decode_wide.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
 }
 
 

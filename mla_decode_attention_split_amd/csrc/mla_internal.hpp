@@ -44,6 +44,7 @@ inline int tile_rows_for(int M) { return M <= 16 ? 16 : M <= 32 ? 32 : M <= 64 ?
 hipError_t launch_sched(const int32_t* seqlens, int batch, int num_parts, int fixed_cost,
                         int32_t* meta, int32_t* num_splits, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, int tile_rows, hipStream_t stream);
+hipError_t launch_decode_wide(const DecodeArgs& a, hipStream_t stream);  // 128-row tiles
 hipError_t launch_combine(CombineArgs a, int num_parts, hipStream_t stream);
 
 }  // namespace mla
