@@ -32,8 +32,10 @@
  * Conventions for every entry point:
  *   - Pointers named "device" are device memory of the current HIP device;
  *     the caller allocates and owns every buffer, including metadata and
- *     workspace.  The library never allocates device memory and keeps no
- *     state between calls except a per-device property cache.
+ *     workspace.  No call allocates device memory.  The library keeps no
+ *     state between calls except a per-device property cache and, for
+ *     mla_decode_noalloc only, a scratch array in device memory that exists
+ *     once per GPU for the life of the process.
  *   - `stream` is a hipStream_t (NULL = the default stream).  Compute calls
  *     only enqueue work: they never synchronize with the host and never read
  *     device memory from the host.
@@ -208,6 +210,29 @@ int mla_decode_splitkv(const void *q, const void *blocked_k, const int32_t *bloc
 int mla_decode_combine(const int32_t *num_splits, int batch, int s_q, int h_q, int h_kv,
                        int num_parts, int dtype, void *out, float *lse, const void *workspace,
                        size_t workspace_bytes, void *stream);
+
+/*
+ * mla_decode without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc).  Same arguments, checks and results as mla_decode
+ * minus workspace / workspace_bytes.  The split partials go to a scratch
+ * array of MLA_NOALLOC_SCRATCH_BYTES that the library holds in device memory,
+ * one copy per GPU, for the life of the process (allocated when the library's
+ * code object is loaded on that GPU); the call itself allocates nothing.
+ *   A call whose partials would not fit (mla_workspace_bytes(batch, M, h_kv,
+ *   num_parts, 512) > MLA_NOALLOC_SCRATCH_BYTES) returns MLA_ERR_WORKSPACE
+ *   and enqueues nothing.
+ *   Nothing in the scratch needs clearing between calls (every value read
+ *   was written earlier in the same call).  All calls on one GPU share its
+ *   scratch: calls that overlap in time on one GPU (different streams, or
+ *   host threads without ordering) race and give wrong results.
+ */
+#define MLA_NOALLOC_SCRATCH_BYTES (128u << 20)
+int mla_decode_noalloc(const void *q, const void *blocked_k, const int32_t *block_table,
+                       const int32_t *cache_seqlens, int batch, int s_q, int h_q, int h_kv,
+                       int d, int dv, int dtype, int num_pages, int page_size, int max_blocks_per_seq,
+                       const int32_t *tile_metadata, int num_parts, const int32_t *num_splits,
+                       int causal, float softmax_scale, void *out, float *lse, void *stream);
 
 #ifdef __cplusplus
 }

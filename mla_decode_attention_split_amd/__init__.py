@@ -23,6 +23,7 @@ import sys
 __all__ = [
     "MlaError", "library_path", "mla_metadata_shape", "mla_tile_shape", "mla_get_metadata",
     "mla_workspace_bytes", "mla_decode", "mla_decode_splitkv", "mla_decode_combine",
+    "mla_decode_noalloc",
     "get_mla_metadata", "flash_mla_with_kvcache",
     "HEAD_DIM", "VALUE_DIM", "PAGE_SIZE",
 ]
@@ -82,6 +83,8 @@ def _load():
     lib.mla_decode_splitkv.restype = i
     lib.mla_decode_combine.argtypes = [p, i, i, i, i, i, i, p, p, p, sz, p]
     lib.mla_decode_combine.restype = i
+    lib.mla_decode_noalloc.argtypes = decode_args[:-3] + [p]
+    lib.mla_decode_noalloc.restype = i
     _lib = lib
     return lib
 
@@ -233,6 +236,42 @@ def mla_decode(q, blocked_k, block_table, cache_seqlens, tile_metadata, num_spli
     out, lse, _ = _decode_call("mla_decode", q, blocked_k, block_table, cache_seqlens,
                                tile_metadata, num_splits, causal, softmax_scale, out, lse,
                                workspace)
+    return out, lse
+
+
+def mla_decode_noalloc(q, blocked_k, block_table, cache_seqlens, tile_metadata, num_splits, *,
+                       causal: bool = False, softmax_scale: float | None = None, out=None, lse=None):
+    """:func:`mla_decode` without a workspace: the split partials go to the
+    library's own device scratch (C call ``mla_decode_noalloc``), for callers
+    that cannot allocate device memory.  Pass ``out`` and ``lse`` to keep the
+    call free of allocations here too."""
+    import torch
+    dtypes = {torch.bfloat16: DTYPE_BF16, torch.float16: DTYPE_FP16}
+    if q.dtype not in dtypes or blocked_k.dtype != q.dtype:
+        raise ValueError("q and blocked_k must both be bfloat16 or both float16")
+    for name, t in (("q", q), ("blocked_k", blocked_k), ("block_table", block_table),
+                    ("cache_seqlens", cache_seqlens), ("tile_metadata", tile_metadata),
+                    ("num_splits", num_splits)):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous CUDA tensor")
+    if q.dim() != 4 or blocked_k.dim() != 4 or block_table.dim() != 2:
+        raise ValueError("q [B,s_q,h_q,d], blocked_k [P,page,h_kv,d], block_table [B,n] expected")
+    B, s_q, h_q, d = q.shape
+    num_pages, page, h_kv, _ = blocked_k.shape
+    scale = float(d) ** -0.5 if softmax_scale is None else float(softmax_scale)
+    dev = q.device
+    with torch.cuda.device(dev):
+        if out is None:
+            out = torch.empty((B, s_q, h_q, VALUE_DIM), dtype=q.dtype, device=dev)
+        elif out.dtype != q.dtype:
+            raise ValueError("out must have q's dtype")
+        if lse is None:
+            lse = torch.empty((B, s_q, h_q), dtype=torch.float32, device=dev)
+        _check(_load().mla_decode_noalloc(
+            q.data_ptr(), blocked_k.data_ptr(), block_table.data_ptr(), cache_seqlens.data_ptr(), B,
+            s_q, h_q, h_kv, d, VALUE_DIM, dtypes[q.dtype], num_pages, page, block_table.shape[1],
+            tile_metadata.data_ptr(), tile_metadata.shape[0], num_splits.data_ptr(),
+            int(bool(causal)), scale, out.data_ptr(), lse.data_ptr(), _stream_of(dev)))
     return out, lse
 
 

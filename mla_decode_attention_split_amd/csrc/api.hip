@@ -353,6 +353,72 @@ int mla_decode_combine(const int32_t* num_splits, int batch, int s_q, int h_q, i
   return ok();
 }
 
+}  // extern "C"
+
+// Scratch of mla_decode_noalloc: the fp32 partial outputs and LSEs of split
+// sequences, in device memory that the library owns (one copy per GPU, held
+// until the process ends).  Host code never uses the array's name as an
+// address: it resolves the address once per device (scratch_of_device) and
+// passes that to the kernels.
+static __device__ __align__(256) unsigned char scratch[MLA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+void* g_scratch_ptr[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+std::once_flag g_scratch_once[kMaxDevices];
+
+// Address of this device's copy of `scratch` (resolved on the first call on
+// the device, with that device current).
+int scratch_of_device(void** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(MLA_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(MLA_ERR_UNSUPPORTED, "device index %d", dev);
+  std::call_once(g_scratch_once[dev], [&]() {
+    void* p = nullptr;
+    g_scratch_err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    g_scratch_ptr[dev] = p;
+  });
+  if (g_scratch_err[dev] != hipSuccess || !g_scratch_ptr[dev])
+    return fail(MLA_ERR_HIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(g_scratch_err[dev]));
+  *ptr = g_scratch_ptr[dev];
+  return MLA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int mla_decode_noalloc(const void* q, const void* blocked_k, const int32_t* block_table,
+                       const int32_t* cache_seqlens, int batch, int s_q, int h_q, int h_kv, int d,
+                       int dv, int dtype, int num_pages, int page_size, int max_blocks_per_seq,
+                       const int32_t* tile_metadata, int num_parts, const int32_t* num_splits,
+                       int causal, float softmax_scale, void* out, float* lse, void* stream) {
+  void* ws = nullptr;
+  int rc = scratch_of_device(&ws);
+  if (rc != MLA_OK) return rc;
+  mla::DecodeArgs a;
+  int tr = 0;
+  rc = prepare_decode(q, blocked_k, block_table, cache_seqlens, batch, s_q, h_q, h_kv, d, dv, dtype,
+                      num_pages, page_size, max_blocks_per_seq, tile_metadata, num_parts, num_splits,
+                      causal, softmax_scale, out, lse, ws, (size_t)MLA_NOALLOC_SCRATCH_BYTES, &a, &tr);
+  if (rc == MLA_ERR_WORKSPACE) {
+    const size_t need = mla_workspace_bytes(batch, s_q * (h_q / h_kv), h_kv, num_parts, dv);
+    return fail(MLA_ERR_WORKSPACE,
+                "mla_decode_noalloc: this call needs %zu bytes of scratch, more than the library's "
+                "%zu (MLA_NOALLOC_SCRATCH_BYTES); use mla_decode with a caller-owned workspace",
+                need, (size_t)MLA_NOALLOC_SCRATCH_BYTES);
+  }
+  if (rc != MLA_OK) return rc;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e = mla::launch_decode(a, tr, st);
+  if (e != hipSuccess) return fail(MLA_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
+  rc = enqueue_combine(a, st);
+  if (rc != MLA_OK) return rc;
+  return ok();
+}
+
 int mla_decode(const void* q, const void* blocked_k, const int32_t* block_table,
                const int32_t* cache_seqlens, int batch, int s_q, int h_q, int h_kv, int d, int dv,
                int dtype, int num_pages, int page_size, int max_blocks_per_seq,

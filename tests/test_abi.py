@@ -16,11 +16,11 @@ CEILING_HEADER = os.path.join(ROOT, "include", "mla_ceiling.h")
 CEILING_LIB = os.path.join(os.path.dirname(mla.library_path()), "libmla_ceiling.so")
 
 # The documented entry points of each library: the boundary's two calls, their
-# sizing helpers and override hook, the split halves of the decode, and the
-# status helpers.
+# sizing helpers and override hook, the split halves of the decode, the decode
+# without a workspace argument, and the status helpers.
 DECODE_API = {"mla_status_string", "mla_last_error", "mla_metadata_shape", "mla_tile_shape",
               "mla_get_metadata", "mla_get_metadata_ex", "mla_workspace_bytes", "mla_decode",
-              "mla_decode_splitkv", "mla_decode_combine"}
+              "mla_decode_splitkv", "mla_decode_combine", "mla_decode_noalloc"}
 CEILING_API = {"mla_ceiling_stream", "mla_ceiling_mfma", "mla_ceiling_last_error"}
 
 
