@@ -979,7 +979,8 @@ __global__ __launch_bounds__(64 * RG * DG, 1) void decode_kernel(
     // WIDE tiles: one iteration finishes stage s - 1 (softmax of its scores,
     // held in sprev, then P V with its keys in ring slot `prev`) while the
     // score MFMAs of stage s (ring slot rd) run.  The first WA score MFMAs
-    // carry the softmax slices; the remaining score MFMAs (one dependent
+    // carry the softmax slices, spread evenly (a slice holds more VALU
+    // work than one MFMA hides); the remaining score MFMAs (one dependent
     // chain) are spread between the 32 independent P V MFMAs.  The K and V
     // fragments of all 68 MFMAs are read through one queue of QD fragments
     // in the order the MFMAs use them, so every LDS read is issued QD MFMAs
@@ -997,7 +998,7 @@ __global__ __launch_bounds__(64 * RG * DG, 1) void decode_kernel(
     };
     constexpr int W_NK = T::WIDE ? KS_W : 1;   // score MFMAs
     constexpr int W_NV = 2 * NT;               // P V MFMAs
-    constexpr int W_WA = 12;                   // score MFMAs before the first P V MFMA
+    constexpr int W_WA = 30;                   // score MFMAs before the first P V MFMA
     constexpr int W_NQR = W_NK - W_WA;
     constexpr int W_NSTEP = W_NK + W_NV;
     auto wide_step = [&](auto hp, auto hc, const char MLA_LDS* __restrict__ rd,
@@ -1044,7 +1045,10 @@ __global__ __launch_bounds__(64 * RG * DG, 1) void decode_kernel(
             }
             if constexpr (g + QD < NS) fq[g % QD] = read_frag(std::integral_constant<int, g + QD>{});
             if constexpr (HP) {
-              if constexpr (g < kSoftSlices) soft_slice(x, ss, g);
+              // the softmax slices spread over the first W_WA - 2 score MFMAs
+              constexpr int SPAN = W_WA - 2;
+              if constexpr ((g * kSoftSlices) % SPAN < kSoftSlices && (g * kSoftSlices) / SPAN < kSoftSlices)
+                soft_slice(x, ss, (g * kSoftSlices) / SPAN);
               if constexpr (g == W_WA - 1) {
                 // the softmax is complete: rescale O if the running max rose
                 // (O is still zero before the first stage), and pack P
