@@ -96,7 +96,7 @@ int default_partition(int q_rows_per_kv_head, int h_kv, int* num_parts, int* fix
                       int* tile_rows, int* m_tiles) {
   int rc = check_rows(q_rows_per_kv_head, h_kv);
   if (rc != MLA_OK) return rc;
-  const int tr = mla::tile_rows_for(q_rows_per_kv_head);
+  const int tr = mla::tile_rows_for(q_rows_per_kv_head, h_kv);
   const int mt = (q_rows_per_kv_head + tr - 1) / tr;
   if (num_parts) {
     int cus = 0;
@@ -234,7 +234,7 @@ int prepare_decode(const void* q, const void* blocked_k, const int32_t* block_ta
   if (workspace_bytes < need)
     return fail(MLA_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", workspace_bytes, need);
 
-  const int tr = mla::tile_rows_for(M);
+  const int tr = mla::tile_rows_for(M, h_kv);
   const size_t pieces = (size_t)batch + (size_t)num_parts;
   const size_t rows = pieces * (size_t)h_kv * (size_t)M;
   a->q = static_cast<const uint16_t*>(q);

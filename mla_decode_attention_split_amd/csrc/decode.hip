@@ -32,7 +32,9 @@ static hipError_t launch_q(const DecodeArgs& a, int tile_rows, hipStream_t strea
     case 16: return launch_t<16, 1, 4, QG, E>(a, stream);
     case 32: return launch_t<16, 2, 2, QG, E>(a, stream);
     case 64: return launch_t<32, 2, 2, QG, E>(a, stream);
-    case 128: return launch_decode_wide(a, stream);
+    case 128:
+      if constexpr (QG) return hipErrorInvalidValue;  // one KV head only
+      else return launch_decode_wide(a, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -112,6 +112,10 @@ __device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t r, unsigned vo
 // writes against its LDS reads itself: an explicit vmcnt wait and a barrier
 // before any slot is read.  M0 holds the LDS address; one wait state
 // separates its write from the load.
+// (clang notes that M0 is a reserved register; the clobber still tells it
+// that the value it may keep there is gone, which is the intent.)
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
 template <bool NT>
 __device__ __forceinline__ void load_lds16_asm(__amdgpu_buffer_rsrc_t r, unsigned voff, char MLA_LDS* dst) {
   const unsigned m0 = (unsigned)(uintptr_t)dst;
@@ -122,6 +126,7 @@ __device__ __forceinline__ void load_lds16_asm(__amdgpu_buffer_rsrc_t r, unsigne
     asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
                  :: "s"(m0), "v"(voff), "s"(r) : "memory", "m0");
 }
+#pragma clang diagnostic pop
 __device__ __forceinline__ int readlane(int v, int lane) { return __builtin_amdgcn_readlane(v, lane); }
 // max of x over lanes l and l ^ 32 (v_permlane32_swap), and l ^ 16
 __device__ __forceinline__ float max_xor32(float x) {
@@ -501,7 +506,31 @@ __global__ __launch_bounds__(64 * RG * DG, 1) void decode_kernel(
   // valid row.  Otherwise (QG) every lane's offset is computed.
   bool pend_q = false;
   bool pend_nt = false;  // the pending position's loads are non-temporal
+  static_assert(!(QG && T::WIDE), "the WIDE tile serves one KV head");
   unsigned qoff[QG ? LPW : 1];
+  // Query row m of the KV head is token m / hpg, head g hpg + m % hpg; the
+  // quotient comes from a float reciprocal (m is below 2^13, so the product
+  // is off by far less than one and truncation errs by at most one) and one
+  // correction.
+  const int q_hq = a.h_q;
+  const float hpg_inv = 1.0f / (float)hpg;
+  auto q_offset = [m_hi, hpg, hpg_inv, q_hq, g, w, lane](int k, int m0) -> unsigned {
+    const int cell = (k * NW + w) * 64 + lane;
+    const int row = cell / kChunksPerRow;
+    const int pc = cell - row * kChunksPerRow;
+    const int m = m0 + row;
+    int t = (int)((float)m * hpg_inv);
+    int h = m - t * hpg;
+    if (h < 0) {
+      t -= 1;
+      h += hpg;
+    } else if (h >= hpg) {
+      t += 1;
+      h -= hpg;
+    }
+    return m < m_hi ? (unsigned)((t * q_hq + g * hpg + h) * kRowBytes + phys_chunk<R>(row, pc) * 16)
+                    : kOutOfRange;
+  };
   // waves past LAST_WAVES skip the stage's last load
   const bool all_loads = T::LAST_WAVES == NW || w < T::LAST_WAVES;
   // Key stages load non-temporally unless other row tiles of the part read
@@ -573,16 +602,7 @@ __global__ __launch_bounds__(64 * RG * DG, 1) void decode_kernel(
         pend = make_rsrc(qseq, a.s_q * a.h_q * kRowBytes);
         pend_q = true;
 #pragma unroll
-        for (int k = 0; k < LPW; ++k) {
-          const int cell = (k * NW + w) * 64 + lane;
-          const int row = cell / kChunksPerRow;
-          const int pc = cell - row * kChunksPerRow;
-          const int m = m0 + row;
-          const int t = m / hpg;
-          qoff[k] = m < m_hi ? (unsigned)((t * a.h_q + g * hpg + (m - t * hpg)) * kRowBytes +
-                                          phys_chunk<R>(row, pc) * 16)
-                             : kOutOfRange;
-        }
+        for (int k = 0; k < LPW; ++k) qoff[k] = q_offset(k, m0);
       } else {
         int rows = m_hi - m0 < kStage ? m_hi - m0 : kStage;
         rows = rows > 0 ? rows : 0;  // the tile's last query stage may be empty
@@ -1049,9 +1069,12 @@ __global__ __launch_bounds__(64 * RG * DG, 1) void decode_kernel(
               constexpr int SPAN = W_WA - 2;
               if constexpr ((g * kSoftSlices) % SPAN < kSoftSlices && (g * kSoftSlices) / SPAN < kSoftSlices)
                 soft_slice(x, ss, (g * kSoftSlices) / SPAN);
-              if constexpr (g == W_WA - 1) {
-                // the softmax is complete: rescale O if the running max rose
-                // (O is still zero before the first stage), and pack P
+              // Right after the slice that decides it (before the
+              // exponentials, which then stay between the score MFMAs
+              // instead of being moved past the branch): rescale O if the
+              // running max rose (O is still zero before the first stage).
+              constexpr int G_RS = (2 * SPAN + kSoftSlices - 1) / kSoftSlices + 1;
+              if constexpr (g == G_RS) {
                 if (ss.rescale && s - 1 > 0) {
 #pragma unroll
                   for (int nt = 0; nt < NT; ++nt) {
@@ -1062,6 +1085,8 @@ __global__ __launch_bounds__(64 * RG * DG, 1) void decode_kernel(
                     else agpr_fence_one<0>(o[nt]);
                   }
                 }
+              }
+              if constexpr (g == W_WA - 1) {  // the softmax is complete: P as MFMA operands
                 pb[0] = __builtin_bit_cast(i16x8, i32x4{(int)ss.pw[0], (int)ss.pw[1], (int)ss.pw[2], (int)ss.pw[3]});
                 pb[1] = __builtin_bit_cast(i16x8, i32x4{(int)ss.pw[4], (int)ss.pw[5], (int)ss.pw[6], (int)ss.pw[7]});
               }

@@ -1,5 +1,5 @@
-// Instances of the decode kernel's WIDE tile: 128 query rows per workgroup,
-// four waves of 32 rows, each wave holding all 512 value dims of its rows
+// Instances of the decode kernel's WIDE tile (one KV head): 128 query rows
+// per workgroup, four waves of 32 rows, each wave holding all 512 value dims of its rows
 // (output accumulators in AGPRs) and contracting all 576 dims of its scores.
 // Built without the VGPR-form MFMA option the other tiles use, so that the
 // output accumulators can live in AGPRs.
@@ -12,21 +12,20 @@ namespace mla {
       const int32_t* __restrict__, const int32_t* __restrict__, uint16_t* __restrict__,      \
       float* __restrict__, float* __restrict__, float* __restrict__, DecodeArgs
 template __global__ void decode_kernel<32, 4, 1, false, Bf16>(MLA_WIDE_PARAMS);
-template __global__ void decode_kernel<32, 4, 1, true, Bf16>(MLA_WIDE_PARAMS);
 template __global__ void decode_kernel<32, 4, 1, false, F16>(MLA_WIDE_PARAMS);
-template __global__ void decode_kernel<32, 4, 1, true, F16>(MLA_WIDE_PARAMS);
 
-template <bool QG, typename E>
+template <typename E>
 static hipError_t launch_w(const DecodeArgs& a, hipStream_t stream) {
-  const int grid = a.num_parts * a.m_tiles * a.h_kv;
-  hipLaunchKernelGGL((decode_kernel<32, 4, 1, QG, E>), dim3(grid), dim3(256), 0, stream, a.q, a.kv,
+  const int grid = a.num_parts * a.m_tiles;
+  hipLaunchKernelGGL((decode_kernel<32, 4, 1, false, E>), dim3(grid), dim3(256), 0, stream, a.q, a.kv,
                      a.block_table, a.seqlens, a.meta, a.out, a.lse, a.o_part, a.lse_part, a);
   return hipGetLastError();
 }
 
+// One KV head (the host picks 64-row tiles for more).
 hipError_t launch_decode_wide(const DecodeArgs& a, hipStream_t stream) {
-  if (a.f16) return a.h_kv == 1 ? launch_w<false, F16>(a, stream) : launch_w<true, F16>(a, stream);
-  return a.h_kv == 1 ? launch_w<false, Bf16>(a, stream) : launch_w<true, Bf16>(a, stream);
+  if (a.h_kv != 1) return hipErrorInvalidValue;
+  return a.f16 ? launch_w<F16>(a, stream) : launch_w<Bf16>(a, stream);
 }
 
 }  // namespace mla

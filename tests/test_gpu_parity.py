@@ -102,12 +102,13 @@ def test_metadata_bitexact_edges(case_name):
 
 def test_metadata_shape_tiles():
     """Tile rows, fixed cost and default part count follow the row count: 64-row
-    tiles up to 64 rows per KV head, 128-row tiles above."""
+    tiles up to 64 rows per KV head, 128-row tiles above with one KV head
+    (64-row tiles with several)."""
     import mla_decode_attention_split_amd as mla
     import torch
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     for M, h_kv, tr in [(16, 1, 16), (32, 1, 32), (64, 1, 64), (65, 1, 128), (256, 1, 128),
-                        (128, 2, 128)]:
+                        (128, 2, 64), (256, 4, 64)]:
         parts, words = mla.mla_metadata_shape(32, M, h_kv)
         tile, m_tiles, fixed = mla.mla_tile_shape(M, h_kv)
         assert words == 8
@@ -297,8 +298,9 @@ def test_two_kv_heads():
 
 @pytest.mark.parametrize("h_q,s_q,h_kv", [(128, 2, 2), (64, 3, 2), (128, 4, 4)])
 def test_kv_heads_many_rows(h_q, s_q, h_kv):
-    """Several KV heads with more than 64 query rows per head (the 128-row,
-    8-wave tile with per-lane query offsets), including a partial row tile."""
+    """Several KV heads with more than 64 query rows per head (64-row tiles,
+    several per head, with per-lane query offsets), including a partial row
+    tile."""
     w = synth.make_workload([700, 129, 64], s_q=s_q, h_q=h_q, h_kv=h_kv, causal=True,
                             seed=27 + h_q + s_q)
     case(w, f"h_kv={h_kv} rows {w.rows_per_kv_head}")
