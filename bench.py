@@ -310,7 +310,7 @@ def ceiling_lib():
         p, i = ctypes.c_void_p, ctypes.c_int
         lib.mla_ceiling_stream.argtypes = [p, i, i, p, i, i, p, p]
         lib.mla_ceiling_stream.restype = i
-        lib.mla_ceiling_mfma.argtypes = [p, i, i, p]
+        lib.mla_ceiling_mfma.argtypes = [p, i, i, i, p]
         lib.mla_ceiling_mfma.restype = i
         lib.mla_ceiling_last_error.restype = ctypes.c_char_p
         _CEILING = lib
@@ -340,10 +340,11 @@ def ceiling_stream(pool, pages, sink):
         int(W), int(P), sink.data_ptr(), _stream_ptr(pool)))
 
 
-def ceiling_mfma(sink, num_workgroups, iters):
-    """num_workgroups x 4 waves of iters x 4 independent 32x32x16 bf16 MFMAs."""
+def ceiling_mfma(sink, num_workgroups, iters, random_operands=False):
+    """num_workgroups x 4 waves of iters x 4 independent 32x32x16 bf16 MFMAs,
+    on constant operands or on random operands that change every MFMA."""
     _ceiling_check(ceiling_lib().mla_ceiling_mfma(sink.data_ptr(), int(num_workgroups), int(iters),
-                                                  _stream_ptr(sink)))
+                                                  int(bool(random_operands)), _stream_ptr(sink)))
 
 
 def span_ms(fn, k, hold_cycles=int(2.4e9 * 0.005)):
@@ -594,19 +595,27 @@ def main():
         ceiling_mfma(fsink, mf_wg, mf_it)
         mfma_ms = span_ms(lambda i: ceiling_mfma(fsink, mf_wg, mf_it), 20)
         mfma_tflops = mf_wg * 4 * mf_it * 4 * 32768 / (mfma_ms * 1e-3) / 1e12
+        ceiling_mfma(fsink, mf_wg, mf_it, True)
+        mfma_r_ms = span_ms(lambda i: ceiling_mfma(fsink, mf_wg, mf_it, True), 20)
+        mfma_r_tflops = mf_wg * 4 * mf_it * 4 * 32768 / (mfma_r_ms * 1e-3) / 1e12
         ceilings = {
             "stream_read": None if stream_tbs is None else {
                 "value": round(stream_tbs, 4), "unit": "TB/s",
                 "what": f"the {primary_name} workload's cache pages through the main kernel's LDS "
                         f"ring, no arithmetic, rotating pool copies"},
             "mfma_bf16": {"value": round(mfma_tflops, 1), "unit": "TFLOP/s",
-                          "what": "independent 32x32x16 bf16 MFMA chains on every SIMD"},
+                          "what": "independent 32x32x16 bf16 MFMA chains on every SIMD, constant operands"},
+            "mfma_bf16_random": {"value": round(mfma_r_tflops, 1), "unit": "TFLOP/s",
+                                 "what": "the same on random bf16 operands that change every MFMA "
+                                         "(the switching power lowers the clock the chip holds)"},
         }
         ceil_p = (stream_tbs * 1e3 if stream_tbs else None) if ctx["hbm_bound"] else mfma_tflops
         ceilings["decode_frac"] = round(ctx["achieved"] / ceil_p, 4) if ceil_p else None
         if second is not None:
             ceilings["compute_bound_decode_frac"] = round(ctx2["achieved"] / mfma_tflops, 4)
-        eprint(f"measured ceilings: paged stream {stream_tbs} TB/s, bf16 MFMA loop {mfma_tflops:.1f} TFLOP/s")
+            ceilings["compute_bound_decode_frac_random"] = round(ctx2["achieved"] / mfma_r_tflops, 4)
+        eprint(f"measured ceilings: paged stream {stream_tbs} TB/s, bf16 MFMA loop {mfma_tflops:.1f} TFLOP/s "
+               f"(random operands {mfma_r_tflops:.1f} TFLOP/s)")
         for key, c in (("primary", ctx), ("compute-bound", ctx2 if second is not None else None)):
             if c is not None:
                 cp = (stream_tbs * 1e3 if stream_tbs else None) if c["hbm_bound"] else mfma_tflops

@@ -43,10 +43,15 @@ int mla_ceiling_stream(const void *pool, int num_pages, int page_bytes, const in
 /*
  * num_workgroups workgroups of 4 waves; each wave runs iters x 4 independent
  * 32x32x16 bf16 MFMAs (32768 flops each).
- *   sink   device float [1], same role as above
+ *   sink             device float [1], same role as above
+ *   random_operands  0: every MFMA reads the same small constant operands;
+ *                    1: the MFMAs cycle through 8 pairs of operand fragments
+ *                    of random bf16 values (magnitudes 1/8 .. 4, random signs
+ *                    and mantissas), so consecutive MFMAs see new inputs as in
+ *                    a kernel that streams cache rows; other values rejected
  * Flops = num_workgroups * 4 * iters * 4 * 32768.
  */
-int mla_ceiling_mfma(float *sink, int num_workgroups, int iters, void *stream);
+int mla_ceiling_mfma(float *sink, int num_workgroups, int iters, int random_operands, void *stream);
 
 /* Thread-local detail of the last failing call on this thread ("" if none). */
 const char *mla_ceiling_last_error(void);

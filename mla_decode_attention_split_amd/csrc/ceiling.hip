@@ -11,7 +11,9 @@
 //     for that access pattern.
 //   * mfma_ceiling_kernel: every wave runs four independent chains of
 //     32x32x16 bf16 MFMAs: the dense bf16 MFMA rate at the clock the chip
-//     holds under that load.
+//     holds under that load, with constant operands or with random operands
+//     that change from one MFMA to the next (the chip draws more power
+//     switching them, and its clock drops under the power limit).
 #include <cstdarg>
 #include <cstdio>
 
@@ -62,29 +64,65 @@ __global__ __launch_bounds__(64 * kCeilWaves, 1) void stream_ceiling_kernel(
   if (acc == 0x9e3779b9u) sink[0] = (int)acc;  // keeps the reads; practically never true
 }
 
-__global__ __launch_bounds__(64 * kCeilWaves) void mfma_ceiling_kernel(float* __restrict__ sink, int iters) {
+// 16-bit pattern of a bf16 value with random sign, exponent in [124, 128]
+// (magnitudes 1/8 .. 4, like N(0,1) samples) and random mantissa, from an
+// integer hash of (seed, key).
+__device__ __forceinline__ short random_bf16(unsigned seed, unsigned key) {
+  unsigned h = (key ^ seed) * 0x9e3779b1u;
+  h ^= h >> 15;
+  h *= 0x85ebca77u;
+  h ^= h >> 13;
+  const unsigned exp = 124u + (h >> 8) % 5u;
+  return (short)(((h >> 31) << 15) | (exp << 7) | (h & 0x7fu));
+}
+
+// RANDOM = false: every MFMA reads the same small constant operands.
+// RANDOM = true: the MFMAs cycle through 8 pairs of random operand fragments,
+// so the inputs of consecutive MFMAs differ in about half of their bits, as
+// they do when a kernel streams fresh cache rows through the MFMAs.
+template <bool RANDOM>
+__global__ __launch_bounds__(64 * kCeilWaves) void mfma_ceiling_kernel(float* __restrict__ sink, int iters,
+                                                                        unsigned seed) {
   const int lane = threadIdx.x & 63;
-  i16x8 a, b;
+  constexpr int NF = RANDOM ? 8 : 1;
+  i16x8 a[NF], b[NF];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    a[i] = (short)(0x3c00 + ((lane + i) & 7));  // small bf16 values
-    b[i] = (short)(0x3c00 + ((lane * 3 + i) & 7));
-  }
+  for (int f = 0; f < NF; ++f)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      if constexpr (RANDOM) {
+        const unsigned key = ((blockIdx.x * blockDim.x + threadIdx.x) * NF + f) * 16 + i;
+        a[f][i] = random_bf16(seed, key);
+        b[f][i] = random_bf16(seed ^ 0x5bd1e995u, key);
+      } else {
+        a[f][i] = (short)(0x3c00 + ((lane + i) & 7));  // small bf16 values
+        b[f][i] = (short)(0x3c00 + ((lane * 3 + i) & 7));
+      }
+    }
   f32x16 acc[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) acc[j] = f32x16{};
-  for (int it = 0; it < iters; ++it) {
+  auto mfma = [&](int j, int fa, int fb) {
+    acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a[fa]),
+                                                     __builtin_bit_cast(bf16x8, b[fb]), acc[j], 0, 0, 0);
+  };
+  int it = 0;
+  if constexpr (RANDOM) {
+    for (; it + 1 < iters; it += 2) {  // two iterations: every fragment pair once
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b),
-                                                       acc[j], 0, 0, 0);
+      for (int m = 0; m < 8; ++m) mfma(m & 3, m, (m + 3) & 7);
+    }
+  }
+  for (; it < iters; ++it) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) mfma(j, j % NF, (j + 3) % NF);
   }
   float s = 0.f;
 #pragma unroll
   for (int j = 0; j < 4; ++j)
 #pragma unroll
     for (int i = 0; i < 16; ++i) s += acc[j][i];
-  if (s == -1.0f) sink[0] = s;  // keeps the chains; never true for these inputs
+  if (s == -1.0f) sink[0] = s;  // keeps the chains; practically never true
 }
 
 }  // namespace mla
@@ -129,12 +167,18 @@ int mla_ceiling_stream(const void* pool, int num_pages, int page_bytes, const in
   return kOk;
 }
 
-int mla_ceiling_mfma(float* sink, int num_workgroups, int iters, void* stream) {
+int mla_ceiling_mfma(float* sink, int num_workgroups, int iters, int random_operands, void* stream) {
   if (!sink) return fail(kInvalid, "null pointer argument");
   if (num_workgroups < 1 || num_workgroups > (1 << 20) || iters < 1 || iters > (1 << 24))
     return fail(kInvalid, "num_workgroups %d, iters %d", num_workgroups, iters);
-  hipLaunchKernelGGL(mla::mfma_ceiling_kernel, dim3(num_workgroups), dim3(64 * mla::kCeilWaves), 0,
-                     static_cast<hipStream_t>(stream), sink, iters);
+  if (random_operands != 0 && random_operands != 1)
+    return fail(kInvalid, "random_operands %d is neither 0 nor 1", random_operands);
+  if (random_operands)
+    hipLaunchKernelGGL(mla::mfma_ceiling_kernel<true>, dim3(num_workgroups), dim3(64 * mla::kCeilWaves), 0,
+                       static_cast<hipStream_t>(stream), sink, iters, 0x2545f491u);
+  else
+    hipLaunchKernelGGL(mla::mfma_ceiling_kernel<false>, dim3(num_workgroups), dim3(64 * mla::kCeilWaves), 0,
+                       static_cast<hipStream_t>(stream), sink, iters, 0u);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(kHip, "mfma ceiling launch: %s", hipGetErrorString(e));
   g_err[0] = '\0';

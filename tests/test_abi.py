@@ -164,7 +164,7 @@ def test_ceiling_helpers_reject_bad_arguments():
     lib = ctypes.CDLL(CEILING_LIB)
     p, i = ctypes.c_void_p, ctypes.c_int
     lib.mla_ceiling_stream.argtypes = [p, i, i, p, i, i, p, p]
-    lib.mla_ceiling_mfma.argtypes = [p, i, i, p]
+    lib.mla_ceiling_mfma.argtypes = [p, i, i, i, p]
     bad = header_constants()["MLA_ERR_INVALID_ARG"]
     page = 64 * 1152
     assert lib.mla_ceiling_stream(None, 8, page, FAKE, 4, 2, FAKE, None) == bad
@@ -172,6 +172,7 @@ def test_ceiling_helpers_reject_bad_arguments():
     assert lib.mla_ceiling_stream(FAKE, (1 << 31) // page + 1, page, FAKE, 4, 2, FAKE, None) == bad
     assert lib.mla_ceiling_stream(FAKE, 8, page, FAKE, 0, 2, FAKE, None) == bad
     assert lib.mla_ceiling_stream(FAKE, 8, page, FAKE, 4, 0, FAKE, None) == bad
-    assert lib.mla_ceiling_mfma(None, 4, 10, None) == bad
-    assert lib.mla_ceiling_mfma(FAKE, 0, 10, None) == bad
-    assert lib.mla_ceiling_mfma(FAKE, 4, 0, None) == bad
+    assert lib.mla_ceiling_mfma(None, 4, 10, 0, None) == bad
+    assert lib.mla_ceiling_mfma(FAKE, 0, 10, 0, None) == bad
+    assert lib.mla_ceiling_mfma(FAKE, 4, 0, 0, None) == bad
+    assert lib.mla_ceiling_mfma(FAKE, 4, 10, 2, None) == bad

@@ -371,6 +371,7 @@ def test_ceiling_helpers_run():
     fsink = torch.zeros(1, dtype=torch.float32, device=dev)
     bench.ceiling_stream(pool, pages, isink)
     bench.ceiling_mfma(fsink, 8, 10)
+    bench.ceiling_mfma(fsink, 8, 11, random_operands=True)
     torch.cuda.synchronize()
     assert int(isink.item()) == 0 and float(fsink.item()) == 0.0
 
