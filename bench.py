@@ -22,8 +22,8 @@ Output: one JSON line on stdout (details on stderr).
               every visible KV row once + q + out + lse + needed table entries
               + cache_seqlens (no padding, re-reads or split partials)
   roofline    the main decode kernel alone: algorithmic bytes per launch /
-              its mean duration (HIP events on the launch stream around K
-              back-to-back launches), against 8 TB/s (or its flops against
+              its mean duration (HIP events on the launch stream around
+              max(K, 200) back-to-back launches), against 8 TB/s (or its flops against
               2.5 PFLOP/s bf16 for MFMA-bound workloads); traffic = HBM bytes
               per launch from the committed rocprofv3 counter summary when it
               matches the current kernel source, else null
@@ -203,7 +203,22 @@ def summarize_profiles(d):
         copy = [(v, n) for name, (v, n) in k.items() if "copyBuffer" in name]
         tot = sum(v * n for v, n in copy) * 1024.0
         cal[c] = {"measured_bytes": tot, "true_bytes": copy_bytes, "scale": copy_bytes / tot}
-    counters = {"kernel_source_digest": kernel_source_digest(),
+    # The digest of the source the profiled runs measured (each run prints it),
+    # so that summaries of older runs are never stamped with a newer digest.
+    import re
+    seen = set()
+    for wl in ("membound", "mtp", "large", "ragged", "hkv2"):
+        ep = os.path.join(d, f"trace_{wl}.err")
+        if os.path.exists(ep):
+            seen |= set(re.findall(r"kernel source digest ([0-9a-f]{16})", open(ep).read()))
+    if len(seen) != 1:
+        raise SystemExit(f"profiled runs name {len(seen)} kernel source digests ({sorted(seen)}); "
+                         f"profile every workload with one build")
+    run_digest = seen.pop()
+    if run_digest != kernel_source_digest():
+        eprint(f"note: the profiled source ({run_digest}) is not the current source "
+               f"({kernel_source_digest()}); the bench will not use these counters")
+    counters = {"kernel_source_digest": run_digest,
                 "calibration": {"kernel": "__amd_rocclr_copyBuffer (torch copy_ of 1 GiB, x5)",
                                 "fetch_scale": round(cal["FETCH_SIZE"]["scale"], 4),
                                 "write_scale": round(cal["WRITE_SIZE"]["scale"], 4)},
@@ -276,6 +291,19 @@ def summarize_profiles(d):
                                  f"trace) = {active / ns:.2f} GHz (the counter window also spans the "
                                  f"dispatch, so for short kernels this overstates the shader clock and "
                                  f"understates the MFMA busy fraction)")
+                if mean.get("SQ_WAVE_CYCLES") and mean.get("SQ_WAVES"):
+                    # SQ_WAVE_CYCLES counts in units of 4 cycles; every tile runs one wave per SIMD
+                    wave_cyc = 4.0 * mean["SQ_WAVE_CYCLES"]
+                    util_w = mean["SQ_VALU_MFMA_BUSY_CYCLES"] / wave_cyc
+                    lines.append(f"  MFMA busy while a wave is resident = SQ_VALU_MFMA_BUSY_CYCLES / (4 x "
+                                 f"SQ_WAVE_CYCLES) = {util_w:.3f} (one wave per SIMD)")
+                    if dec:
+                        per_wave = wave_cyc / mean["SQ_WAVES"]
+                        lines.append(f"  cycles per wave = 4 x SQ_WAVE_CYCLES / SQ_WAVES = {per_wave:.0f}; over the "
+                                     f"mean kernel time: {per_wave / ns:.2f} GHz (a lower bound of the shader "
+                                     f"clock: waves live shorter than the kernel)")
+                    if entry:
+                        entry["mfma_busy_frac_resident"] = round(util_w, 4)
                 if entry:
                     entry["mfma_busy_frac"] = round(util, 4)
             if mean.get("SQ_INSTS_LDS"):
@@ -373,6 +401,7 @@ def measure_workload(name, args, dev, primary):
     w = synth.named_workload(name, dtype=args.dtype)
     nbytes, flops = algorithmic_units(w)
     M, h_kv = w.rows_per_kv_head, w.h_kv
+    eprint(f"[{name}] kernel source digest {kernel_source_digest()}")
     pool_bytes = w.kcache.nbytes
     copies = max(1, int(np.ceil(args.rotate_bytes / pool_bytes)))
     eprint(f"[{name}] B={w.batch} s_q={w.s_q} h_q={w.h_q} h_kv={h_kv} causal={w.causal} "
@@ -433,10 +462,15 @@ def measure_workload(name, args, dev, primary):
     # Pass 2: the main kernel alone, launched back to back over the same
     # metadata (computed once, outside the timed region), HIP events at both
     # ends on the stream the kernel runs on; mean launch duration = span / K.
+    # K is at least 200 launches: the chip's clock under load settles over
+    # milliseconds (it is power-limited), and a short window would weigh the
+    # first launches after the idle hold too much.
+    k_dec = max(args.steps, 200)
+    hold_dec = int(2.4e9 * (1.5 * enqueue_s * k_dec + 0.01))
     dec_ms = span_ms(lambda i: mla.mla_decode_splitkv(q, kvs[i % copies], bt, sl, meta, splits,
                                                       causal=w.causal, softmax_scale=w.scale,
                                                       out=out, lse=lse, workspace=ws),
-                     args.steps, hold_cycles)
+                     k_dec, hold_dec)
     # Pass 3: the metadata call and the combine alone (same buffers).
     meta_ms = span_ms(lambda i: mla.mla_get_metadata(sl, M, h_kv, tile_metadata=meta,
                                                      num_splits=splits), 200)
@@ -457,7 +491,7 @@ def measure_workload(name, args, dev, primary):
     roof["traffic"] = counter_traffic(name)
     eprint(f"[{name}] host enqueue {enqueue_s * 1e6:.1f} us/step")
     eprint(f"[{name}] step {ms_per_step * 1e3:.2f} us -> {step_tbs:.3f} TB/s, {step_tflops:.1f} TFLOP/s")
-    eprint(f"[{name}] decode kernel {dec_ms * 1e3:.2f} us mean over {args.steps} back-to-back launches "
+    eprint(f"[{name}] decode kernel {dec_ms * 1e3:.2f} us mean over {k_dec} back-to-back launches "
            f"-> {achieved:.1f} {roof['unit']} ({roof['frac'] * 100:.1f}% of peak)")
     eprint(f"[{name}] metadata call {meta_ms * 1e3:.2f} us, combine {comb_ms * 1e3:.2f} us (each alone); "
            f"timed step equals mla_decode bitwise: {same}")
@@ -472,6 +506,7 @@ def measure_workload(name, args, dev, primary):
         "tbs": round(step_tbs, 4),
         "tflops": round(step_tflops, 3),
         "decode_kernel_us": round(dec_ms * 1e3, 3),
+        "decode_kernel_launches": k_dec,
         "roofline": roof,
         "parts_us": {"metadata": round(meta_ms * 1e3, 3), "decode": round(dec_ms * 1e3, 3),
                      "combine": round(comb_ms * 1e3, 3)},
@@ -640,6 +675,7 @@ def main():
         "config": block["config"],
         "tflops": block["tflops"],
         "decode_kernel_us": block["decode_kernel_us"],
+        "decode_kernel_launches": block["decode_kernel_launches"],
         "roofline": block["roofline"],
         "parts_us": block["parts_us"],
         "step_equals_mla_decode": block["step_equals_mla_decode"],
