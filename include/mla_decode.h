@@ -114,12 +114,15 @@ int mla_tile_shape(int q_rows_per_kv_head, int h_kv, int *tile_rows, int *m_tile
  * One device kernel (one workgroup) reads cache_seqlens and writes the
  * partition; nothing is copied to the host.
  *
- * Partition rule (sequences are cut only at multiples of 32 keys):
- *   U_b = ceil(N_b / 32); cost_b = U_b + fixed_cost; C_b = sum_{b'<b} cost_b';
- *   T = ceil(C_B / num_parts).  Unit i of sequence b belongs to part
- *   floor((C_b + fixed_cost + i) / T); a sequence with N_b = 0 gets one empty
- *   piece in part floor((C_b + fixed_cost - 1) / T).  A piece is the run of
- *   one sequence's units inside one part.  num_parts and fixed_cost are the
+ * Partition rule (sequences are cut only at multiples of 32 keys), on a
+ * cost line counted in half units with f = fixed_cost:
+ *   U_b = ceil(N_b / 32); sequence b occupies 2 U_b + 2 f positions (f for
+ *   its start, two per unit, f for its end); C_b = sum_{b'<b} (2 U_b' + 2 f);
+ *   T = max(2, ceil(C_B / num_parts)).  Unit i of sequence b belongs to part
+ *   floor((C_b + f + 2 i + 1) / T) (the part of its midpoint); a sequence
+ *   with N_b = 0 gets one empty piece in part floor((C_b + f) / T).  A piece
+ *   is the run of one sequence's units inside one part; the pieces of a
+ *   sequence sit in consecutive parts.  num_parts and fixed_cost are the
  *   values mla_metadata_shape and mla_tile_shape report.
  *
  *   cache_seqlens  device int32 [batch], every N_b >= 0 (not checked on host)

@@ -4,8 +4,10 @@
 // Block scheduling (FlashMLA explainer, jsxs2.com, section 3.1) and the
 // get_mla_metadata call (cnblogs FlashMLA notes, section 6) are named on the
 // pages; the partition rule is this library's, stated in mla_decode.h:
-// cost-interval partition at 32-key granularity with a per-sequence fixed
-// cost, so that ragged batches spread over the compute units.
+// cost-interval partition at 32-key granularity on a line counted in half
+// units, with a per-sequence fixed cost split over the sequence's two ends
+// and every unit placed at its midpoint, so that ragged batches spread over
+// the compute units and equal sequences split into equal pieces.
 //
 // The kernel is latency-bound (a few hundred integers), so it is built to
 // touch global memory once per input and once per output: cache_seqlens is
@@ -14,6 +16,13 @@
 // part of cost position x is floor(x / T), so "part <= p" is "x < (p+1) T").
 // Integer divisions (software-emulated on the GPU) are only taken a constant
 // number of times per thread.
+//
+// Positions, for sequence b with U_b units and fixed cost f (half units):
+//   C_b = sum over b' < b of (2 U_b' + 2 f)
+//   KF_b = C_b + f + 1 (first unit's midpoint), KL_b = C_b + f + 2 U_b - 1
+//   (last unit's midpoint); both C_b + f for a sequence with no unit.
+//   Part p holds positions [p T, (p+1) T), T = max(2, ceil(C_B / num_parts)).
+//   Units of b before part p: max(0, ceil((p T - C_b - f - 1) / 2)).
 #include "mla_common.hpp"
 #include "mla_internal.hpp"
 
@@ -74,13 +83,13 @@ __global__ __launch_bounds__(NT) void sched_kernel(const int32_t* __restrict__ s
     if (b < batch) {
       const int n = seqlens[b];
       if constexpr (kSlInLds) SL_lds[b] = n;
-      local += units_of(n) + fc;
+      local += 2 * units_of(n) + 2 * fc;
     }
   }
   long long total;
   long long base = block_exclusive_scan<NT>(local, scratch, &total);
   long long T = (total + num_parts - 1) / num_parts;
-  if (T < 1) T = 1;
+  if (T < 2) T = 2;
 
   // 2. prefix costs, and pieces per sequence = last part - first part + 1.
   long long pieces = 0;
@@ -89,10 +98,10 @@ __global__ __launch_bounds__(NT) void sched_kernel(const int32_t* __restrict__ s
     if (b < batch) {
       C[b] = base;
       const long long u = units_of(SL(b));
-      const long long first = u > 0 ? (base + fc) / T : (base + fc - 1) / T;
-      const long long last = (base + fc + u - 1) / T;
+      const long long first = (base + fc + (u > 0 ? 1 : 0)) / T;
+      const long long last = (base + fc + (u > 0 ? 2 * u - 1 : 0)) / T;
       pieces += last - first + 1;
-      base += u + fc;
+      base += 2 * u + 2 * fc;
     }
   }
   if (tid == 0) C[batch] = total;
@@ -105,8 +114,8 @@ __global__ __launch_bounds__(NT) void sched_kernel(const int32_t* __restrict__ s
       if constexpr (kSlInLds) NS_lds[b] = (int32_t)pbase;
       const long long cb = C[b];
       const long long u = units_of(SL(b));
-      const long long first = u > 0 ? (cb + fc) / T : (cb + fc - 1) / T;
-      const long long last = (cb + fc + u - 1) / T;
+      const long long first = (cb + fc + (u > 0 ? 1 : 0)) / T;
+      const long long last = (cb + fc + (u > 0 ? 2 * u - 1 : 0)) / T;
       pbase += last - first + 1;
     }
   }
@@ -118,12 +127,14 @@ __global__ __launch_bounds__(NT) void sched_kernel(const int32_t* __restrict__ s
   __syncthreads();  // C and num_splits complete
 
   // Cost positions that decide a sequence's first and last part:
-  //   last part  = floor(KL_b / T), KL_b = C_{b+1} - 1
-  //   first part = floor(KF_b / T), KF_b = C_b + fc (or C_b + fc - 1 if empty)
-  auto KL = [&](int b) -> long long { return C[b + 1] - 1; };
+  //   last part  = floor(KL_b / T), first part = floor(KF_b / T)
+  auto KL = [&](int b) -> long long {
+    const long long cb = C[b], u2 = C[b + 1] - cb - 2 * fc;  // 2 U_b
+    return cb + fc + (u2 > 0 ? u2 - 1 : 0);
+  };
   auto KF = [&](int b) -> long long {
     const long long cb = C[b];
-    return C[b + 1] - cb - fc > 0 ? cb + fc : cb + fc - 1;
+    return cb + fc + (C[b + 1] - cb - 2 * fc > 0 ? 1 : 0);
   };
 
   // 3. per part: first sequence with last part >= p, last with first part <= p.
@@ -145,15 +156,16 @@ __global__ __launch_bounds__(NT) void sched_kernel(const int32_t* __restrict__ s
     const int be = lo;
     i32x4 w0 = {0, 0, -1, 0}, w1 = {0, 0, 0, 0};
     if (bb < batch && be >= 0 && bb <= be) {
-      const long long ub = C[bb + 1] - C[bb] - fc;
-      const long long ue = C[be + 1] - C[be] - fc;
+      const long long ub = (C[bb + 1] - C[bb]) / 2 - fc;
+      const long long ue = (C[be + 1] - C[be]) / 2 - fc;
       long long u_begin = 0, u_end = 0;
-      if (ub > 0) {
-        u_begin = lo_key - C[bb] - fc;
-        if (u_begin < 0) u_begin = 0;
+      if (ub > 0) {  // units of bb whose midpoint lies before this part
+        const long long a = lo_key - C[bb] - fc - 1;
+        u_begin = a > 0 ? (a + 1) / 2 : 0;
       }
-      if (ue > 0) {
-        u_end = hi_key - C[be] - fc;
+      if (ue > 0) {  // units of be whose midpoint lies before the next part
+        const long long a = hi_key - C[be] - fc - 1;
+        u_end = a > 0 ? (a + 1) / 2 : 0;
         if (u_end > ue) u_end = ue;
       }
       long long tok_end = u_end * kStage;
@@ -196,7 +208,7 @@ __global__ __launch_bounds__(kSmallThreads) void sched_small_kernel(
     if (b < batch) {
       const int n = seqlens[b];
       SL[b] = n;
-      local += units_of(n) + fc;
+      local += 2 * units_of(n) + 2 * fc;
     }
   }
   long long total;
@@ -205,7 +217,7 @@ __global__ __launch_bounds__(kSmallThreads) void sched_small_kernel(
   const bool narrow = total < 0x7fffffffLL;
   long long T = narrow ? (long long)(((unsigned)total + (unsigned)num_parts - 1u) / (unsigned)num_parts)
                        : (total + num_parts - 1) / num_parts;
-  if (T < 1) T = 1;
+  if (T < 2) T = 2;
   // floor(x / T): q = high half of x * floor((2^32 - 1) / T) is at most 2
   // below the quotient for x < 2^31; the remainder loop corrects it exactly.
   const unsigned T32 = (unsigned)T;
@@ -226,12 +238,12 @@ __global__ __launch_bounds__(kSmallThreads) void sched_small_kernel(
     if (b < batch) {
       C[b] = base;
       const long long u = units_of(SL[b]);
-      const int first = u > 0 ? part_of(base + fc) : part_of(base + fc - 1);
-      const int last = part_of(base + fc + u - 1);
+      const int first = part_of(base + fc + (u > 0 ? 1 : 0));
+      const int last = part_of(base + fc + (u > 0 ? 2 * u - 1 : 0));
       FP[b] = first;
       LP[b] = last;
       pieces += last - first + 1;
-      base += u + fc;
+      base += 2 * u + 2 * fc;
     }
   }
   if (tid == 0) C[batch] = total;
@@ -270,15 +282,16 @@ __global__ __launch_bounds__(kSmallThreads) void sched_small_kernel(
     i32x4 w0 = {0, 0, -1, 0}, w1 = {0, 0, 0, 0};
     if (bb < batch && be >= 0 && bb <= be) {
       const long long lo_key = (long long)p * T, hi_key = (long long)(p + 1) * T;
-      const long long ub = C[bb + 1] - C[bb] - fc;
-      const long long ue = C[be + 1] - C[be] - fc;
+      const long long ub = (C[bb + 1] - C[bb]) / 2 - fc;
+      const long long ue = (C[be + 1] - C[be]) / 2 - fc;
       long long u_begin = 0, u_end = 0;
-      if (ub > 0) {
-        u_begin = lo_key - C[bb] - fc;
-        if (u_begin < 0) u_begin = 0;
+      if (ub > 0) {  // units of bb whose midpoint lies before this part
+        const long long a = lo_key - C[bb] - fc - 1;
+        u_begin = a > 0 ? (a + 1) / 2 : 0;
       }
-      if (ue > 0) {
-        u_end = hi_key - C[be] - fc;
+      if (ue > 0) {  // units of be whose midpoint lies before the next part
+        const long long a = hi_key - C[be] - fc - 1;
+        u_end = a > 0 ? (a + 1) / 2 : 0;
         if (u_end > ue) u_end = ue;
       }
       long long tok_end = u_end * kStage;

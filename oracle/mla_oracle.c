@@ -297,15 +297,20 @@ int mla_oracle_decode_split(const uint16_t *q, const uint16_t *kcache, const int
  * small blocks run in parallel, and get_mla_metadata returns
  * tile_scheduler_metadata and num_splits from cache_seqlens).  The pages give
  * no rule; this is the rule the library documents, written out step by step.
- * A "unit" is unit_tokens consecutive keys of one sequence.
+ * A "unit" is unit_tokens consecutive keys of one sequence; f = fixed_cost.
  *
- *   1. U_b = ceil(N_b / unit_tokens) units; cost_b = U_b + fixed_cost.
- *   2. C_b = cost_0 + ... + cost_{b-1};  total = C_B;
- *      T = ceil(total / num_parts)  (cost per part).
- *   3. Part p owns the cost interval [p*T, (p+1)*T).  Unit i of sequence b
- *      sits at cost C_b + fixed_cost + i, so it belongs to part
- *      floor((C_b + fixed_cost + i) / T).  A sequence with no unit gets one
- *      empty piece in part floor((C_b + fixed_cost - 1) / T).
+ *   1. U_b = ceil(N_b / unit_tokens) units.  On a cost line counted in half
+ *      units, sequence b occupies 2 U_b + 2 f positions: f for its start-up
+ *      work, two per unit, f for its finishing work (one fixed cost of f
+ *      units per sequence, half at each end).
+ *   2. S_b = sum over b' < b of (2 U_b' + 2 f); TOT = S_B.  Every part
+ *      spans T = max(2, ceil(TOT / num_parts)) positions: position x belongs
+ *      to part floor(x / T).  (T >= 2 puts at least one unit midpoint into
+ *      every part that lies inside a sequence's units, so the pieces of a
+ *      sequence sit in consecutive parts.)
+ *   3. Unit i of sequence b is placed at its midpoint, x = S_b + f + 2 i + 1,
+ *      and belongs to that position's part.  A sequence with no unit gets
+ *      one empty piece in the part of x = S_b + f.
  *   4. A piece is the run of one sequence's units inside one part; pieces of
  *      a sequence sit in consecutive parts.  num_splits[b+1] - num_splits[b]
  *      is the number of pieces of sequence b (num_splits[0] = 0).
@@ -315,84 +320,81 @@ int mla_oracle_decode_split(const uint16_t *q, const uint16_t *kcache, const int
  *      N_bb, N_be, and num_splits[be] (the partial slot of be's piece, whose
  *      split index is 0).  A part with no piece stores first = 0, last = -1
  *      and zeros elsewhere.
+ * Every unit is visited one by one here (no closed form), so the result pins
+ * a scheduler that computes piece bounds arithmetically.
  */
+
 int mla_oracle_schedule(const int32_t *seqlens, int B, int unit_tokens, int num_parts,
                         int fixed_cost, int32_t *tile_meta, int32_t *num_splits) {
   if (B < 0 || unit_tokens < 1 || num_parts < 1 || fixed_cost < 1) return ORACLE_ERR_ARG;
-  long *C = (long *)malloc(sizeof(long) * (size_t)(B + 1));
-  long *first = (long *)malloc(sizeof(long) * (size_t)(B > 0 ? B : 1));
-  long *last = (long *)malloc(sizeof(long) * (size_t)(B > 0 ? B : 1));
-  long *units = (long *)malloc(sizeof(long) * (size_t)(B > 0 ? B : 1));
-  if (!C || !first || !last || !units) {
-    free(C);
-    free(first);
-    free(last);
-    free(units);
-    return ORACLE_ERR_NOMEM;
+  for (int b = 0; b < B; ++b)
+    if (seqlens[b] < 0) return ORACLE_ERR_ARG;
+  for (long i = 0; i < (long)num_parts * 8; ++i) tile_meta[i] = 0;
+  for (int p = 0; p < num_parts; ++p) tile_meta[(long)p * 8 + 2] = -1; /* empty until a piece lands */
+  if (B == 0) {
+    num_splits[0] = 0;
+    return ORACLE_OK;
   }
-  C[0] = 0;
-  for (int b = 0; b < B; ++b) {
-    if (seqlens[b] < 0) {
-      free(C);
-      free(first);
-      free(last);
-      free(units);
-      return ORACLE_ERR_ARG;
-    }
-    units[b] = ((long)seqlens[b] + unit_tokens - 1) / unit_tokens;
-    C[b + 1] = C[b] + units[b] + fixed_cost;
-  }
-  long total = C[B];
-  long T = (total + num_parts - 1) / num_parts;
-  if (T < 1) T = 1;
+  const long f = fixed_cost;
+  long tot = 0;
+  for (int b = 0; b < B; ++b) tot += 2 * (((long)seqlens[b] + unit_tokens - 1) / unit_tokens) + 2 * f;
+  long T = (tot + num_parts - 1) / num_parts;
+  if (T < 2) T = 2;
+
+  /* Walk every unit in order; each change of part (or of sequence) starts a
+   * new piece.  For every piece remember its sequence, part, split index and
+   * key range; then fill the per-part words from the pieces. */
+  long S = 0;
+  int pieces = 0;
   num_splits[0] = 0;
   for (int b = 0; b < B; ++b) {
-    if (units[b] > 0) {
-      first[b] = (C[b] + fixed_cost) / T;
-      last[b] = (C[b] + fixed_cost + units[b] - 1) / T;
+    const long n = seqlens[b];
+    const long u = (n + unit_tokens - 1) / unit_tokens;
+    int split = 0;
+    if (u == 0) {
+      const long p = (S + f) / T;
+      int32_t *w = tile_meta + p * 8;
+      if (w[2] < 0) { /* the part's first piece */
+        w[0] = b;
+        w[1] = 0;
+        w[4] = pieces;
+        w[5] = (int32_t)n;
+      }
+      w[2] = b;
+      w[3] = 0;
+      w[6] = (int32_t)n;
+      ++pieces;
+      split = 1;
     } else {
-      first[b] = last[b] = (C[b] + fixed_cost - 1) / T;
-    }
-    num_splits[b + 1] = num_splits[b] + (int32_t)(last[b] - first[b] + 1);
-  }
-  for (int p = 0; p < num_parts; ++p) {
-    int32_t *w = tile_meta + (long)p * 8;
-    int bb = -1, be = -1;
-    for (int b = 0; b < B; ++b) {
-      if (first[b] <= p && p <= last[b]) {
-        if (bb < 0) bb = b;
-        be = b;
+      long cur = -1;
+      for (long i = 0; i < u; ++i) {
+        const long p = (S + f + 2 * i + 1) / T;
+        const long key_lo = i * unit_tokens;
+        const long key_hi = (i + 1) * unit_tokens < n ? (i + 1) * unit_tokens : n;
+        int32_t *w = tile_meta + p * 8;
+        if (p != cur) { /* a new piece of sequence b in part p */
+          cur = p;
+          if (w[2] < 0) { /* and the part's first piece */
+            w[0] = b;
+            w[1] = (int32_t)key_lo;
+            w[4] = pieces;
+            w[5] = (int32_t)n;
+          }
+          w[2] = b;
+          w[6] = (int32_t)n;
+          ++pieces;
+          ++split;
+        }
+        w[3] = (int32_t)key_hi;
       }
     }
-    for (int i = 0; i < 8; ++i) w[i] = 0;
-    if (bb < 0) {
-      w[0] = 0;
-      w[2] = -1;
-      continue;
-    }
-    long u_begin = 0, u_end = 0;
-    if (units[bb] > 0) {
-      u_begin = (long)p * T - C[bb] - fixed_cost;
-      if (u_begin < 0) u_begin = 0;
-    }
-    if (units[be] > 0) {
-      u_end = (long)(p + 1) * T - C[be] - fixed_cost;
-      if (u_end > units[be]) u_end = units[be];
-    }
-    long tok_end = u_end * unit_tokens;
-    if (tok_end > seqlens[be]) tok_end = seqlens[be];
-    w[0] = bb;
-    w[1] = (int32_t)(u_begin * unit_tokens);
-    w[2] = be;
-    w[3] = (int32_t)tok_end;
-    w[4] = num_splits[bb] + (int32_t)(p - first[bb]); /* partial slot of the first piece */
-    w[5] = seqlens[bb];
-    w[6] = seqlens[be];
-    w[7] = num_splits[be]; /* partial slot of the last piece (its first split) */
+    num_splits[b + 1] = num_splits[b] + split;
+    S += 2 * u + 2 * f;
   }
-  free(C);
-  free(first);
-  free(last);
-  free(units);
+  /* word 7: num_splits[be], known once every sequence is walked */
+  for (int p = 0; p < num_parts; ++p) {
+    int32_t *w = tile_meta + (long)p * 8;
+    if (w[2] >= 0) w[7] = num_splits[w[2]];
+  }
   return ORACLE_OK;
 }

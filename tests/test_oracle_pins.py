@@ -339,19 +339,21 @@ def test_bad_page_index_is_rejected():
 # --------------------------------------------------------------------------
 
 def enumerate_parts(seqlens, num_parts, fixed_cost, unit):
-    """Part of every unit, unit by unit, straight from the cost-interval rule."""
+    """Part of every unit, unit by unit, straight from the cost-interval rule:
+    a line in half units, each sequence's fixed cost split over its two ends,
+    each unit at its midpoint, parts of T = max(2, ceil(total / num_parts))
+    positions."""
     units = [(int(n) + unit - 1) // unit for n in seqlens]
-    total = sum(u + fixed_cost for u in units)
-    T = max(1, -(-total // num_parts))
-    cost = 0
+    total = sum(2 * u + 2 * fixed_cost for u in units)
+    T = max(2, -(-total // num_parts))
+    pos = 0
     where = []
     for u in units:
-        cost += fixed_cost
         if u == 0:
-            where.append([(cost - 1) // T])
+            where.append([(pos + fixed_cost) // T])
         else:
-            where.append([(cost + i) // T for i in range(u)])
-        cost += u
+            where.append([(pos + fixed_cost + 2 * i + 1) // T for i in range(u)])
+        pos += 2 * u + 2 * fixed_cost
     return units, where, T
 
 
@@ -401,11 +403,24 @@ def test_schedule_matches_unit_enumeration(seed):
             assert all(where[b][i // unit] == p for i in range(lo, hi))
         assert covered == list(range(int(lens[b])))     # exact cover of the keys, in order
     assert len(got) == ns[-1]
-    # balance: no part holds more than T units of keys
+    # balance: no part holds more units of keys than fit in T half units
     per_part = np.zeros(num_parts, dtype=np.int64)
     for (b, k), (p, lo, hi) in got.items():
         per_part[p] += -(-(hi - lo) // unit)
-    assert per_part.max() <= T
+    assert per_part.max() <= (T + 1) // 2
+
+
+def test_schedule_even_halves():
+    """With the fixed cost split over both ends of a sequence, equal sequences
+    over twice as many parts are cut exactly in half: every part holds one
+    piece of half a sequence (hand-checked: 128 x 4096 keys, 32-key units,
+    fixed cost 5, 256 parts: T = 128 x 266 / 256 = 133 half units)."""
+    lens = np.full(128, 4096)
+    meta, ns = oracle.schedule(lens, num_parts=256, fixed_cost=5, unit_tokens=32)
+    np.testing.assert_array_equal(ns, np.arange(0, 257, 2))
+    for p in range(256):
+        b, half = divmod(p, 2)
+        assert tuple(meta[p, :4]) == (b, 2048 * half, b, 2048 * (half + 1))
 
 
 def test_schedule_rejects_bad_arguments():
