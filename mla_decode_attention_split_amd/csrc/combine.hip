@@ -31,10 +31,17 @@ constexpr float kLog2e = 1.44269504088896340736f;
 constexpr float kLn2c = 0.69314718055994530942f;
 constexpr int kCombineWaves = 4;  // waves per workgroup
 constexpr int kUnroll = 16;       // pieces loaded per trip
+constexpr int kUnrollFew = 4;     // ... when sequences average at most 4 pieces
 constexpr int kShareMin = 4;      // shared-row grid: more pieces than this, 4 waves per row
 constexpr int kSharePieces = 16;  // pick the shared-row grid at this many pieces per sequence
 
+// UNROLL pieces per trip: 16, or 4 when the batch averages at most 4 pieces
+// per sequence (then 32 instead of 128 registers hold a trip's rows, and
+// about four times as many waves fit on a SIMD to keep more rows in flight).
+// Pieces are added in index order either way, so both give the same bits.
+template <int UNROLL>
 __global__ __launch_bounds__(64 * kCombineWaves) void combine_kernel(CombineArgs a) {
+  constexpr int kUnroll = UNROLL;
   const int b = blockIdx.z;
   const int g = blockIdx.y;
   const int s0 = sload_i32(a.num_splits + b);
@@ -159,7 +166,12 @@ __global__ __launch_bounds__(64 * kCombineWaves) void combine_kernel(CombineArgs
 hipError_t launch_combine(CombineArgs a, int num_parts, hipStream_t stream) {
   a.share_grid = (long long)num_parts >= (long long)kSharePieces * a.batch ? 1 : 0;
   dim3 grid(a.share_grid ? a.M : (a.M + kCombineWaves - 1) / kCombineWaves, a.h_kv, a.batch);
-  hipLaunchKernelGGL(combine_kernel, grid, dim3(64 * kCombineWaves), 0, stream, a);
+  // pieces per sequence <= 1 + num_parts / batch on average
+  const bool few = !a.share_grid && (long long)num_parts <= (long long)(kUnrollFew - 1) * a.batch;
+  if (few)
+    hipLaunchKernelGGL(combine_kernel<kUnrollFew>, grid, dim3(64 * kCombineWaves), 0, stream, a);
+  else
+    hipLaunchKernelGGL(combine_kernel<kUnroll>, grid, dim3(64 * kCombineWaves), 0, stream, a);
   return hipGetLastError();
 }
 

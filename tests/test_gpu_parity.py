@@ -154,6 +154,22 @@ def test_metadata_bitexact():
         np.testing.assert_array_equal(splits.cpu().numpy(), rsplits)
 
 
+def test_metadata_even_halves():
+    """Equal sequences over twice as many parts: the device scheduler cuts each
+    one exactly in half (one piece per part), as the oracle's rule does."""
+    import mla_decode_attention_split_amd as mla
+    import torch
+    log("[case] metadata even halves: B=128 N=4096 parts=256 fixed=5")
+    lens = np.full(128, 4096, dtype=np.int32)
+    meta, splits = mla.mla_get_metadata(torch.from_numpy(lens).cuda(), 128, 1, num_parts=256,
+                                        fixed_cost=5)
+    torch.cuda.synchronize()
+    rmeta, rsplits = oracle.schedule(lens, num_parts=256, fixed_cost=5, unit_tokens=32)
+    np.testing.assert_array_equal(meta.cpu().numpy(), rmeta)
+    np.testing.assert_array_equal(splits.cpu().numpy(), rsplits)
+    np.testing.assert_array_equal(rsplits, np.arange(0, 257, 2))
+
+
 @pytest.mark.parametrize("num_parts", [1, 7, 64, None])
 def test_split_count_does_not_change_result(num_parts):
     lens = [5000, 33, 1, 700, 64, 2048, 0, 3000]
