@@ -1,6 +1,6 @@
 // Main paged MLA decode kernel for gfx950 (CDNA4): the kernel template.
-// Instantiated in decode.hip (tiles of up to 64 query rows and the 8-wave
-// 128-row tile) and decode_wide.hip (the 4-wave 128-row tile).
+// Instantiated in decode.hip (tiles of up to 64 query rows) and
+// decode_wide.hip (the 128-row tile of one KV head).
 //
 // What it computes (cnblogs FlashMLA notes, sections 2 and 4): for every query
 // row, blockwise scores against the 576-wide cached latent rows of its
@@ -13,9 +13,8 @@
 // partial outputs).
 //
 // Design (gfx950):
-//   * One workgroup per CU: 4 waves for tiles of up to 64 query rows, 8 waves
-//     (two per SIMD) for 128-row tiles.  The part's stages (query rows, then
-//     32-key blocks, per piece) stream through a ring of 4 (8 waves: 3) LDS
+//   * One workgroup per CU, 4 waves (one per SIMD).  The part's stages (query
+//     rows, then 32-key blocks, per piece) stream through a ring of 4 LDS
 //     slots of 36 KB with 16-byte buffer loads straight into LDS.  Every ring
 //     position is loaded with the same number of instructions per wave; lanes
 //     with nothing to load address past their buffer's range, which costs no
@@ -25,22 +24,23 @@
 //     and last sequence, and the page indices of the part are loaded into
 //     registers (lane i holds entry i) while the query stage is already in
 //     flight.
-//   * Each wave owns R query rows (R = 16 or 32) and 512 / DG value dims.
-//     Scores are computed transposed, S^T = K Q^T, with K from LDS (A
+//   * Scores are computed transposed, S^T = K Q^T, with K from LDS (A
 //     operand) and Q^T resident in registers (B operand); the MFMA result is
 //     already laid out as the B operand P^T of O^T = V^T P^T.  V^T comes from
 //     LDS through transposed 8-byte reads (ds_read_b64_tr_b16).
-//   * Split-K scores: the DG waves of a row group each contract an interleaved
-//     share of the 576 dims (and, with DG = 4, one of the two 16-key blocks),
-//     then exchange fp32 partial scores through LDS and add them in a fixed
-//     order, so every wave of the group holds bit-identical scores.
-//   * Software pipeline (4-wave tiles): in the iteration of key block s a
-//     wave computes the partial scores of block s while it finishes block
-//     s - 1 (partial-score sum, softmax, P V); the MFMAs of one overlap the
-//     vector work of the other, and one barrier per stage serves both the ring
-//     and the exchange.  8-wave tiles have no registers for that; they run
-//     each stage in order and rely on the second wave of the SIMD instead,
-//     and keep the Q^T fragments of the rope dims in LDS.
+//   * Tiles of up to 64 rows (split-K): each wave owns R query rows (R = 16
+//     or 32) and 512 / DG value dims; the DG waves of a row group each
+//     contract an interleaved share of the 576 dims (and, with DG = 4, one of
+//     the two 16-key blocks), then exchange fp32 partial scores through LDS
+//     and add them in a fixed order, so every wave of the group holds
+//     bit-identical scores.
+//   * The 128-row tile (WIDE): each wave owns 32 rows and all 512 value dims
+//     (output accumulators in the AGPRs) and contracts all 576 score dims
+//     itself, so nothing is exchanged.
+//   * Software pipeline: in the iteration of key block s a wave computes the
+//     scores of block s while it finishes block s - 1 (softmax, P V); the
+//     MFMAs of one overlap the vector work of the other, and one barrier per
+//     stage serves both the ring and the exchange.
 //   * Softmax in fp32 in the log2 domain; the running max is raised only when
 //     a row's new max exceeds it by more than kTau (then O and l are
 //     rescaled).  P is rounded to bf16 for the MFMA and a second row sum adds
@@ -224,7 +224,7 @@ __device__ __forceinline__ i16x8 cat(i16x4 a, i16x4 b) {
 }
 
 // Tile shape.  R rows per wave (32x32x16 MFMA for R = 32, 16x16x32 for
-// R = 16), RG row groups x DG value-dim groups = 4 or 8 waves.
+// R = 16), RG row groups x DG value-dim groups = 4 waves (one per SIMD).
 template <int R, int RG, int DG>
 struct Tile {
   static constexpr int NW = RG * DG;
@@ -233,10 +233,8 @@ struct Tile {
   // (its output accumulators fill the AGPRs) and contracts all 576 dims of
   // its scores itself, so no partial scores are exchanged.
   static constexpr bool WIDE = DG == 1;
-  // 16-byte loads per lane per stage; with 8 waves the last load is issued
-  // by the first LAST_WAVES waves only (36 = 4 x 8 + 4)
-  static constexpr int LPW = (kLoadsPerStage + NW - 1) / NW;
-  static constexpr int LAST_WAVES = kLoadsPerStage - (LPW - 1) * NW;
+  // 16-byte loads per lane per stage (36 per stage = 4 waves x 9)
+  static constexpr int LPW = kLoadsPerStage / NW;
   static constexpr int KSTEPS = R == 32 ? 36 : 18;       // score k-steps over 576 dims
   static constexpr int KSPLIT = WIDE ? 1 : 2;            // k-step interleave among DG waves
   static constexpr int KBSPLIT = DG / KSPLIT;            // 16-key blocks split among waves (R = 16)
@@ -249,28 +247,20 @@ struct Tile {
   // 16-row tiles double-buffer the exchange; 32-row tiles have room for one
   // buffer and separate its reads from the next writes with a barrier; WIDE
   // tiles exchange nothing.
-  static constexpr int XCH_BUFS = WIDE ? 0 : (R == 32 || NW == 8) ? 1 : 2;
-  // 8-wave 32-row tiles (128 rows, two waves per SIMD) are not software
-  // pipelined: each stage's scores, softmax and P V run in order, and the
-  // other wave of the SIMD fills the gaps.  Their ring has 3 slots (stage s
-  // is computed while s + 1 and s + 2 load), which leaves room for the
-  // 8-wave exchange buffer.
-  static constexpr bool FLAT = NW == 8 && R == 32;
-  static constexpr int SLOTS = FLAT ? 3 : kSlots;
-  static constexpr int RING_BYTES = SLOTS * kStageBytes;
-  // FLAT and WIDE tiles keep the Q^T fragments of the rope dims (the last
-  // QR_STEPS k-steps of each wave) in LDS instead of registers
-  static constexpr int QR_STEPS = FLAT ? 2 : WIDE ? 4 : 0;
+  static constexpr int XCH_BUFS = WIDE ? 0 : R == 32 ? 1 : 2;
+  static constexpr int RING_BYTES = kSlots * kStageBytes;
+  // WIDE tiles keep the Q^T fragments of the rope dims (the last QR_STEPS
+  // k-steps of each wave) in LDS instead of registers
+  static constexpr int QR_STEPS = WIDE ? 4 : 0;
   static constexpr int QREG_STEPS = KS_W - QR_STEPS;     // Q^T k-steps held in registers
   static constexpr int QR_BYTES = NW * QR_STEPS * 1024;
   static constexpr int NQ = (BM + kStage - 1) / kStage;  // query stages per piece
   static constexpr int QK_MFMA = KS_W * KB_W;
   static constexpr int PV_MFMA = R == 32 ? 2 * NT : NT;
   static constexpr int NSLOT = QK_MFMA + PV_MFMA;        // points where loads are issued
-  static_assert(NW == 4 || NW == 8, "four or eight waves per workgroup");
+  static_assert(NW == 4 && LPW * NW == kLoadsPerStage, "four waves per workgroup, 9 loads each");
   static_assert(WIDE ? (R == 32 && NW == 4) : (DG >= 2 && DG % 2 == 0),
                 "split-K tiles, or the 4-wave WIDE tile of 32-row waves");
-  static_assert(LAST_WAVES > 0 && LAST_WAVES <= NW, "stage loads split over the waves");
   static_assert(KS_W * KSPLIT == KSTEPS && KBSPLIT * KSPLIT == DG, "score split");
   static_assert(R == 16 || KBSPLIT == 1, "key-block split only for 16-row tiles");
   static_assert(NSLOT >= LPW, "one load per issue point at most");
@@ -297,7 +287,7 @@ __global__ __launch_bounds__(64 * RG * DG, 1) void decode_kernel(
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int lane = tid & 63;
-  // this wave's Q^T rope fragments (FLAT tiles): step j at qr0 + 1024 j
+  // this wave's Q^T rope fragments (WIDE tiles): step j at qr0 + 1024 j
   char MLA_LDS* qr0 = T::QR_STEPS > 0 ? xch0 + T::XCH_BUFS * T::XCH_ONE + w * T::QR_STEPS * 1024 + lane * 16
                                       : lds;
   const int rg = w / DG;
@@ -467,7 +457,7 @@ __global__ __launch_bounds__(64 * RG * DG, 1) void decode_kernel(
   // ---- stage stream -----------------------------------------------------------
   // For every non-empty piece: NQ query stages (32 rows of the tile each, same
   // swizzled row layout as the keys), then the piece's key stages.  Stream
-  // position c uses ring slot c % SLOTS; position c + 2 is loaded while
+  // position c uses ring slot c % 4; position c + 2 is loaded while
   // position c is computed.  Past the end of the stream the loads are out of
   // range.
   // Cursor of the stream: piece lj, query stage lq, key token ltok (end lhi),
@@ -531,8 +521,6 @@ __global__ __launch_bounds__(64 * RG * DG, 1) void decode_kernel(
     return m < m_hi ? (unsigned)((t * q_hq + g * hpg + h) * kRowBytes + phys_chunk<R>(row, pc) * 16)
                     : kOutOfRange;
   };
-  // waves past LAST_WAVES skip the stage's last load
-  const bool all_loads = T::LAST_WAVES == NW || w < T::LAST_WAVES;
   // Key stages load non-temporally unless other row tiles of the part read
   // the same pages; query stages never do (the pieces of a sequence split
   // over many parts all read its query rows).  The 4-wave 64-row tile (two
@@ -540,7 +528,6 @@ __global__ __launch_bounds__(64 * RG * DG, 1) void decode_kernel(
   // batch and keeps the default policy.
   const bool nt_kv = a.m_tiles == 1 && (T::WIDE || !(R == 32 && NW == 4));
   auto fire = [&](int k) {
-    if (k == LPW - 1 && !all_loads) return;
     if constexpr (QG) load_lds16(pend, pend_q ? qoff[k] : loff[k], pend_dst + k * NW * 1024, pend_nt);
     else load_lds16(pend, loff[k], pend_dst + k * NW * 1024, pend_nt);
   };
@@ -550,7 +537,6 @@ __global__ __launch_bounds__(64 * RG * DG, 1) void decode_kernel(
     auto fire_nt = [&](auto nt) {
 #pragma unroll
       for (int k = 0; k < LPW; ++k) {
-        if (k == LPW - 1 && !all_loads) continue;
         const unsigned vo = QG && pend_q ? qoff[QG ? k : 0] : loff[k];
         if constexpr (T::WIDE) load_lds16_asm<decltype(nt)::value>(pend, vo, pend_dst + k * NW * 1024);
         else load_lds16(pend, vo, pend_dst + k * NW * 1024, decltype(nt)::value);
@@ -619,16 +605,12 @@ __global__ __launch_bounds__(64 * RG * DG, 1) void decode_kernel(
   fire_all();
 
   int cstage = 0;
-  auto slot_of = [&](int c) {
-    if constexpr (T::SLOTS == 3) return lds + (c % 3) * kStageBytes;  // c >= 0 here
-    else return lds + (c & (kSlots - 1)) * kStageBytes;
-  };
+  auto slot_of = [&](int c) { return lds + (c & (kSlots - 1)) * kStageBytes; };
   // Wait for stream position cstage (position cstage + 1 may stay in flight),
   // then a barrier: the stage and the previous iteration's partial scores are
   // visible to all waves, and the slot refilled next has been read by all.
   auto stage_ready = [&]() {
-    if (all_loads) wait_vmcnt<LPW>();
-    else wait_vmcnt<LPW - 1>();
+    wait_vmcnt<LPW>();
     block_barrier();
   };
   // query rows of this wave inside its query stage
@@ -943,59 +925,6 @@ __global__ __launch_bounds__(64 * RG * DG, 1) void decode_kernel(
       else fire_from(T::QK_MFMA);
     };
 
-    // FLAT tiles: a stage's partial scores, their exchange with the other
-    // wave of the row group (each wave keeps its own partial and adds the
-    // partner's; the two sums are bit-identical since fp32 addition commutes),
-    // softmax and P V.
-    auto flat_scores = [&](const char MLA_LDS* __restrict__ rd) -> f32x16 {
-      f32x16 sacc = f32x16{};
-      if constexpr (T::FLAT) {
-        constexpr int NK = KS_W;
-        constexpr int KP = 2;  // K fragments read ahead (registers are tight at 2 waves per SIMD)
-        i16x8 kf[KP];
-#pragma unroll
-        for (int i = 0; i < KP; ++i) kf[i] = lds_read_b128(rd + kstep_off(i));
-        __builtin_amdgcn_sched_barrier(0);
-        i16x8 qrf[T::QR_STEPS];
-#pragma unroll
-        for (int i = 0; i < NK; ++i) {
-          if (i == T::QREG_STEPS - 4) {  // the rope fragments, a few MFMAs ahead
-#pragma unroll
-            for (int j = 0; j < T::QR_STEPS; ++j) qrf[j] = lds_read_b128(qr0 + 1024 * j);
-          }
-          if (i < T::QREG_STEPS) sacc = E::mfma32(kf[i % KP], qf[i < T::QREG_STEPS ? i : 0], sacc);
-          else sacc = E::mfma32(kf[i % KP], qrf[i >= T::QREG_STEPS ? i - T::QREG_STEPS : 0], sacc);
-          if (i + KP < NK) kf[i % KP] = lds_read_b128(rd + kstep_off(i + KP));
-          fire_slot(i);
-          __builtin_amdgcn_sched_barrier(0);
-        }
-#pragma unroll
-        for (int qd = 0; qd < 4; ++qd)
-          lds_write_f4(xch0 + w * 4096 + qd * 1024 + lane * 16,
-                       f32x4{sacc[4 * qd], sacc[4 * qd + 1], sacc[4 * qd + 2], sacc[4 * qd + 3]});
-      }
-      return sacc;
-    };
-    // Full scores of stage sp (own partial + the partner's), softmax and P V
-    // with the keys of ring slot st.
-    auto flat_finish = [&](const f32x16& own, int sp, const char MLA_LDS* __restrict__ st, int first_slot) {
-      if constexpr (T::FLAT) {
-        float x[SREGS];
-        const char MLA_LDS* pp = xch0 + (w ^ 1) * 4096 + lane * 16;
-#pragma unroll
-        for (int qd = 0; qd < 4; ++qd) {
-          const f32x4 u = lds_read_f4(pp + qd * 1024);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) x[4 * qd + e] = own[4 * qd + e] + u[e];
-        }
-        prep(x, sp);
-        SoftState ss;
-#pragma unroll
-        for (int j = 0; j < kSoftSlices; ++j) soft_slice(x, ss, j);
-        pv(ss.pw, ss.rescale, ss.alpha, sp, st, first_slot);
-      }
-    };
-
     // WIDE tiles: one iteration finishes stage s - 1 (softmax of its scores,
     // held in sprev, then P V with its keys in ring slot `prev`) while the
     // score MFMAs of stage s (ring slot rd) run.  The first WA score MFMAs
@@ -1128,15 +1057,7 @@ __global__ __launch_bounds__(64 * RG * DG, 1) void decode_kernel(
       }
       using F = std::false_type;
       using Tr = std::true_type;
-      if constexpr (T::FLAT) {
-        for (int s = 0; s < nst; ++s, ++cstage) {
-          stage_ready();
-          plan(slot_of(cstage + 2));
-          const f32x16 sc = flat_scores(slot_of(cstage));
-          block_barrier();  // the partial scores are exchanged
-          flat_finish(sc, s, slot_of(cstage), T::QK_MFMA);
-        }
-      } else if constexpr (T::WIDE) {
+      if constexpr (T::WIDE) {
         stage_ready();
         plan(slot_of(cstage + 2));
         fire_all();
