@@ -48,7 +48,9 @@
  *     in [0, num_pages); ceil(N/64) <= max_blocks_per_seq; the metadata was
  *     produced by mla_get_metadata(_ex) for the same cache_seqlens, rows and
  *     h_kv.  Cache rows at positions >= N and table entries >= ceil(N/64) are
- *     never used and may hold anything (NaN included).
+ *     never used and may hold anything (NaN included).  A needed table entry
+ *     outside [0, num_pages) is read as a page of zeros (no memory outside
+ *     the pool is touched); the result is then that of a zero page.
  */
 #ifndef MLA_DECODE_H
 #define MLA_DECODE_H

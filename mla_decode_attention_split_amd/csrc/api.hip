@@ -254,6 +254,7 @@ int prepare_decode(const void* q, const void* blocked_k, const int32_t* block_ta
   a->h_kv = h_kv;
   a->M = M;
   a->max_blocks = max_blocks_per_seq;
+  a->num_pages = num_pages;
   a->num_parts = num_parts;
   a->m_tiles = (M + tr - 1) / tr;
   a->causal = causal ? 1 : 0;

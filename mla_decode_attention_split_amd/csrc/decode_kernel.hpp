@@ -573,9 +573,12 @@ __global__ __launch_bounds__(64 * RG * DG, 1) void decode_kernel(
       else page = sload_i32(block_table + (long long)(bb + lj) * a.max_blocks + (ltok >> 6));
       // Rows past the end of the sequence are out of the buffer's range, so
       // they arrive as zeros: their V rows then contribute exactly nothing
-      // (cache memory past the end may hold anything, NaN included).
-      const int rows = lhi - ltok < kStage ? lhi - ltok : kStage;
-      pend = make_rsrc(kv_bytes + page * page_bytes + lhalf * half_bytes, rows * row_stride);
+      // (cache memory past the end may hold anything, NaN included).  A
+      // table entry outside the pool loads nothing either: the stage reads
+      // as a page of zeros, and no memory outside the pool is touched.
+      const bool page_ok = (unsigned)page < (unsigned)a.num_pages;
+      const int rows = !page_ok ? 0 : lhi - ltok < kStage ? lhi - ltok : kStage;
+      pend = make_rsrc(kv_bytes + (page_ok ? page : 0) * page_bytes + lhalf * half_bytes, rows * row_stride);
       lpos += lhalf;
       lhalf ^= 1;
       ltok += kStage;

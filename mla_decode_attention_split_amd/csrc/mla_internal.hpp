@@ -20,6 +20,7 @@ struct DecodeArgs {
   float* o_part;              // [max_pieces, h_kv, M, 512]
   float* lse_part;            // [max_pieces, h_kv, M]
   int batch, s_q, h_q, h_kv, M, max_blocks, num_parts, m_tiles;
+  int num_pages;              // pages in blocked_k: a table entry outside [0, num_pages) reads zeros
   int causal;
   int xcd_map;                // 1: the m-tiles / KV heads of one part share an XCD
   float scale_log2;           // softmax_scale * log2(e)
@@ -37,8 +38,6 @@ struct CombineArgs {
   int f16;         // 1: out is fp16; 0: bf16
 };
 
-// Query rows per workgroup for M rows per KV head (16, 32 or 64; larger M
-// takes several 64-row tiles).
 // Query rows per workgroup for M rows per KV head.  The 128-row tile serves
 // one KV head only (with several heads its query-row offsets would not fit
 // in its registers); more rows per head use 64-row tiles.

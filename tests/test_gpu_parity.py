@@ -344,6 +344,32 @@ def test_pool_past_4gib():
     check_parity(out, lse, *ref(w), what="pool past 4 GiB")
 
 
+@pytest.mark.parametrize("h_q,s_q", [(16, 1), (64, 1), (128, 2)])
+def test_table_entry_outside_pool_reads_zeros(h_q, s_q):
+    """A block_table entry equal to num_pages reads as a page of zeros.  The
+    pool handed to the library is a view of one page fewer than the allocated
+    tensor, so the entry still points into allocated memory (filled with 3.0):
+    reading it would change the result, not fault.  Reference: the oracle on
+    the same table with page num_pages made of zeros.  Covers the 16-row,
+    64-row and 128-row tiles."""
+    import dataclasses
+    import torch
+    w = synth.make_workload([300, 200], s_q=s_q, h_q=h_q, causal=s_q > 1, seed=81 + h_q)
+    case(w, f"table entry outside the pool, h_q={h_q}")
+    q, kv, bt, sl = to_device(w)
+    P = kv.shape[0]
+    alloc = torch.full((P + 1,) + tuple(kv.shape[1:]), 3.0, dtype=kv.dtype, device=kv.device)
+    alloc[:P] = kv
+    bt_bad = bt.clone()
+    bt_bad[0, 1] = P  # the second page of sequence 0 (keys 64..127 of 300)
+    out, lse = run_gpu(w, tensors=(q, alloc[:P], bt_bad, sl))
+    zero_page = np.zeros((1,) + w.kcache.shape[1:], dtype=w.kcache.dtype)
+    table = w.block_table.copy()
+    table[0, 1] = P
+    w_ref = dataclasses.replace(w, kcache=np.concatenate([w.kcache, zero_page]), block_table=table)
+    check_parity(out, lse, *ref(w_ref), what=f"entry outside the pool, h_q={h_q}")
+
+
 @pytest.mark.parametrize("lens,s_q,h_q", [([131072], 1, 16), ([65536, 1000], 2, 64)])
 def test_long_sequences(lens, s_q, h_q):
     """Sequences of 64K and 128K keys, split over every part of the default
