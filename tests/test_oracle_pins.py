@@ -410,6 +410,27 @@ def test_schedule_matches_unit_enumeration(seed):
     assert per_part.max() <= (T + 1) // 2
 
 
+@pytest.mark.parametrize("lens,num_parts,fixed_cost", [([32, 0, 64, 100], 256, 1),
+                                                        ([1], 1000, 1), ([0, 0, 5000], 64, 3)])
+def test_schedule_tiny_total(lens, num_parts, fixed_cost):
+    """Far more parts than cost positions (T is held at 2 half units): every
+    sequence's pieces still sit in consecutive parts and cover its keys once."""
+    lens = np.asarray(lens)
+    meta, ns = oracle.schedule(lens, num_parts=num_parts, fixed_cost=fixed_cost, unit_tokens=32)
+    units, where, T = enumerate_parts(lens, num_parts, fixed_cost, 32)
+    assert T == 2 or sum(2 * u + 2 * fixed_cost for u in units) > 2 * num_parts
+    got = pieces_from_meta(meta, lens, ns)
+    for b in range(len(lens)):
+        parts = sorted(set(where[b]))
+        assert parts == list(range(parts[0], parts[-1] + 1))
+        keys = []
+        for k in range(ns[b + 1] - ns[b]):
+            p, lo, hi = got[(b, k)]
+            assert p == parts[k]
+            keys.extend(range(lo, hi))
+        assert keys == list(range(int(lens[b])))
+
+
 def test_schedule_even_halves():
     """With the fixed cost split over both ends of a sequence, equal sequences
     over twice as many parts are cut exactly in half: every part holds one
