@@ -155,9 +155,9 @@ int mla_get_metadata_ex(const int32_t *cache_seqlens, int batch, int q_rows_per_
                         int32_t *tile_metadata, int32_t *num_splits, void *stream,
                         int num_parts_override, int fixed_cost_override);
 
-/* Bytes of device workspace mla_decode needs (fp32 partial outputs and
- * their lse for up to batch + num_parts pieces); 0 on invalid arguments
- * (including dv != 512). */
+/* Bytes of device workspace mla_decode needs (the partial outputs of up to
+ * batch + num_parts pieces, 512 values per row in the 16-bit element type of
+ * q, then their fp32 lse); 0 on invalid arguments (including dv != 512). */
 size_t mla_workspace_bytes(int batch, int q_rows_per_kv_head, int h_kv, int num_parts, int dv);
 
 /*
@@ -198,7 +198,9 @@ int mla_decode(const void *q, const void *blocked_k, const int32_t *block_table,
  *
  * mla_decode_splitkv: same arguments and checks as mla_decode; enqueues only
  * the main kernel.  Sequences with one piece get their final out/lse; the
- * others leave fp32 partials in the workspace.
+ * others leave partials in the workspace (each piece's normalised output
+ * row in the element type of q, a convex combination of value rows, and its
+ * fp32 lse; the combine merges them in fp32).
  *
  * mla_decode_combine: merges the partials of sequences with several pieces
  * into out/lse (a sequence with one piece is left untouched).  batch, s_q,

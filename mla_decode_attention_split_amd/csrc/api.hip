@@ -180,7 +180,7 @@ size_t mla_workspace_bytes(int batch, int q_rows_per_kv_head, int h_kv, int num_
     return 0;
   const size_t pieces = (size_t)batch + (size_t)num_parts;
   const size_t rows = pieces * (size_t)h_kv * (size_t)q_rows_per_kv_head;
-  size_t o_bytes = rows * MLA_VALUE_DIM * sizeof(float);
+  size_t o_bytes = rows * MLA_VALUE_DIM * sizeof(uint16_t);
   size_t l_bytes = rows * sizeof(float);
   l_bytes = (l_bytes + 255) & ~(size_t)255;
   return o_bytes + l_bytes;
@@ -245,9 +245,9 @@ int prepare_decode(const void* q, const void* blocked_k, const int32_t* block_ta
   a->num_splits = num_splits;
   a->out = static_cast<uint16_t*>(out);
   a->lse = lse;
-  a->o_part = static_cast<float*>(workspace);
+  a->o_part = static_cast<uint16_t*>(workspace);
   a->lse_part = reinterpret_cast<float*>(static_cast<char*>(workspace) +
-                                         rows * MLA_VALUE_DIM * sizeof(float));
+                                         rows * MLA_VALUE_DIM * sizeof(uint16_t));
   a->batch = batch;
   a->s_q = s_q;
   a->h_q = h_q;
@@ -337,9 +337,9 @@ int mla_decode_combine(const int32_t* num_splits, int batch, int s_q, int h_q, i
   const size_t rows = ((size_t)batch + (size_t)num_parts) * (size_t)h_kv * (size_t)M;
   mla::DecodeArgs a{};
   a.num_splits = num_splits;
-  a.o_part = const_cast<float*>(static_cast<const float*>(workspace));
+  a.o_part = const_cast<uint16_t*>(static_cast<const uint16_t*>(workspace));
   a.lse_part = reinterpret_cast<float*>(const_cast<char*>(static_cast<const char*>(workspace)) +
-                                        rows * MLA_VALUE_DIM * sizeof(float));
+                                        rows * MLA_VALUE_DIM * sizeof(uint16_t));
   a.out = static_cast<uint16_t*>(out);
   a.lse = lse;
   a.batch = batch;
@@ -356,7 +356,7 @@ int mla_decode_combine(const int32_t* num_splits, int batch, int s_q, int h_q, i
 
 }  // extern "C"
 
-// Scratch of mla_decode_noalloc: the fp32 partial outputs and LSEs of split
+// Scratch of mla_decode_noalloc: the 16-bit partial outputs and fp32 LSEs of split
 // sequences, in device memory that the library owns (one copy per GPU, held
 // until the process ends).  Host code never uses the array's name as an
 // address: it resolves the address once per device (scratch_of_device) and

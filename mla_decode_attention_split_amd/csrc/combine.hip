@@ -1,15 +1,17 @@
-// Split combine: merge the fp32 partial outputs of a sequence's pieces by
-// their log-sum-exp (the merge of partial outputs, cnblogs FlashMLA notes,
+// Split combine: merge the partial outputs of a sequence's pieces by their
+// log-sum-exp (the merge of partial outputs, cnblogs FlashMLA notes,
 // section 4; num_splits from get_mla_metadata, section 6):
 //     L = ln sum_k exp(lse_k),   out = sum_k exp(lse_k - L) * o_k.
 // Pieces with lse_k = -inf (no visible key) weigh nothing; if every piece is
 // empty the row gets out = 0 and lse = -inf.  Sequences with a single piece
 // were written directly by the main kernel and are skipped here.
 //
+// Partial rows are 16-bit (the element type of out: each is a convex
+// combination of value rows, rounded once); LSEs and all sums are fp32.
 // The kernel is latency-bound, so each wave makes two dependent trips to
 // memory: the split range (scalar loads), then the piece LSEs (lane k holds
 // piece k) together with the partial rows of up to kUnroll pieces (64 lanes x
-// 8 value dims, two 16-byte loads per lane and piece).  Two layouts, chosen
+// 8 value dims, one 16-byte load per lane and piece).  Two layouts, chosen
 // per sequence from its piece count (so every row of a sequence is summed in
 // the same order):
 //   * one wave per query row, 4 rows per workgroup;
@@ -22,6 +24,8 @@
 // wave layout only the first ceil(M / 4) of them work); the host picks it
 // when the batch averages many pieces per sequence, since idle workgroups
 // cost dispatch time.
+#include <type_traits>
+
 #include "mla_common.hpp"
 #include "mla_internal.hpp"
 
@@ -35,11 +39,27 @@ constexpr int kUnrollFew = 4;     // ... when sequences average at most 4 pieces
 constexpr int kShareMin = 4;      // shared-row grid: more pieces than this, 4 waves per row
 constexpr int kSharePieces = 16;  // pick the shared-row grid at this many pieces per sequence
 
+// 8 partial values of one 16-byte load, widened to fp32 (exact).
+template <typename E>
+__device__ __forceinline__ void widen8(const uint4& u, float* f) {
+  const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if constexpr (std::is_same<E, F16>::value) {
+      f[2 * i] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w[i] & 0xffffu));
+      f[2 * i + 1] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w[i] >> 16));
+    } else {
+      f[2 * i] = __uint_as_float(w[i] << 16);
+      f[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+  }
+}
+
 // UNROLL pieces per trip: 16, or 4 when the batch averages at most 4 pieces
-// per sequence (then 32 instead of 128 registers hold a trip's rows, and
-// about four times as many waves fit on a SIMD to keep more rows in flight).
-// Pieces are added in index order either way, so both give the same bits.
-template <int UNROLL>
+// per sequence (then 16 instead of 64 registers hold a trip's rows, and more
+// waves fit on a SIMD to keep more rows in flight).  Pieces are added in
+// index order either way, so both give the same bits.
+template <int UNROLL, typename E>
 __global__ __launch_bounds__(64 * kCombineWaves) void combine_kernel(CombineArgs a) {
   constexpr int kUnroll = UNROLL;
   const int b = blockIdx.z;
@@ -70,17 +90,12 @@ __global__ __launch_bounds__(64 * kCombineWaves) void combine_kernel(CombineArgs
 
   // Issue the first trip's partial rows with the LSE loads (lane k holds
   // the LSE of piece c + k), then reduce.
-  const float* o_row = a.o_part + r0 * kValueDim + lane * 8;
+  const uint16_t* o_row = a.o_part + r0 * kValueDim + lane * 8;
   const int n0 = p_hi - p_lo < kUnroll ? p_hi - p_lo : kUnroll;
-  float4 x[kUnroll][2];
+  uint4 x[kUnroll];
 #pragma unroll
-  for (int j = 0; j < kUnroll; ++j) {
-    if (j < n0) {
-      const float4* src = reinterpret_cast<const float4*>(o_row + (p_lo + j) * stride * kValueDim);
-      x[j][0] = src[0];
-      x[j][1] = src[1];
-    }
-  }
+  for (int j = 0; j < kUnroll; ++j)
+    if (j < n0) x[j] = *reinterpret_cast<const uint4*>(o_row + (p_lo + j) * stride * kValueDim);
   auto lse_at = [&](int c) -> float {
     return c + lane < nsplit ? lse_row[(c + lane) * stride] : -INFINITY;
   };
@@ -94,9 +109,11 @@ __global__ __launch_bounds__(64 * kCombineWaves) void combine_kernel(CombineArgs
     float sum = 0.f;
     for (int c = 0; c < nsplit; c += 64) sum += fast_exp2(((c == 0 ? v0 : lse_at(c)) - mx) * kLog2e);
     L = mx + fast_log2(wave_allsum_f32(sum)) * kLn2c;
-    auto add = [&](const float4* xj, float wk) {
-      acc[0] += wk * xj[0].x; acc[1] += wk * xj[0].y; acc[2] += wk * xj[0].z; acc[3] += wk * xj[0].w;
-      acc[4] += wk * xj[1].x; acc[5] += wk * xj[1].y; acc[6] += wk * xj[1].z; acc[7] += wk * xj[1].w;
+    auto add = [&](const uint4& xj, float wk) {
+      float v[8];
+      widen8<E>(xj, v);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] += wk * v[i];
     };
     // Trips start at multiples of kUnroll, so the pieces of one trip share a
     // 64-piece chunk and one weight register (lane k: piece c + k), read with a
@@ -114,13 +131,8 @@ __global__ __launch_bounds__(64 * kCombineWaves) void combine_kernel(CombineArgs
     for (int k0 = p_lo + kUnroll; k0 < p_hi; k0 += kUnroll) {
       const float wl = weights(k0);
 #pragma unroll
-      for (int j = 0; j < kUnroll; ++j) {
-        if (k0 + j < p_hi) {
-          const float4* src = reinterpret_cast<const float4*>(o_row + (k0 + j) * stride * kValueDim);
-          x[j][0] = src[0];
-          x[j][1] = src[1];
-        }
-      }
+      for (int j = 0; j < kUnroll; ++j)
+        if (k0 + j < p_hi) x[j] = *reinterpret_cast<const uint4*>(o_row + (k0 + j) * stride * kValueDim);
 #pragma unroll
       for (int j = 0; j < kUnroll; ++j)
         if (k0 + j < p_hi) add(x[j], row_total_f32(wl, (k0 + j) & 63));
@@ -148,17 +160,10 @@ __global__ __launch_bounds__(64 * kCombineWaves) void combine_kernel(CombineArgs
   const int h = g * hpg + m % hpg;
   const long long out_row = ((long long)b * a.s_q + t) * a.h_q + h;
   uint4 pk;
-  if (a.f16) {
-    pk.x = pack_f16(acc[0], acc[1]);
-    pk.y = pack_f16(acc[2], acc[3]);
-    pk.z = pack_f16(acc[4], acc[5]);
-    pk.w = pack_f16(acc[6], acc[7]);
-  } else {
-    pk.x = pack_bf16(acc[0], acc[1]);
-    pk.y = pack_bf16(acc[2], acc[3]);
-    pk.z = pack_bf16(acc[4], acc[5]);
-    pk.w = pack_bf16(acc[6], acc[7]);
-  }
+  pk.x = E::pack(acc[0], acc[1]);
+  pk.y = E::pack(acc[2], acc[3]);
+  pk.z = E::pack(acc[4], acc[5]);
+  pk.w = E::pack(acc[6], acc[7]);
   *reinterpret_cast<uint4*>(a.out + out_row * kValueDim + lane * 8) = pk;
   if (lane == 0) a.lse[out_row] = L;
 }
@@ -168,10 +173,15 @@ hipError_t launch_combine(CombineArgs a, int num_parts, hipStream_t stream) {
   dim3 grid(a.share_grid ? a.M : (a.M + kCombineWaves - 1) / kCombineWaves, a.h_kv, a.batch);
   // pieces per sequence <= 1 + num_parts / batch on average
   const bool few = !a.share_grid && (long long)num_parts <= (long long)(kUnrollFew - 1) * a.batch;
-  if (few)
-    hipLaunchKernelGGL(combine_kernel<kUnrollFew>, grid, dim3(64 * kCombineWaves), 0, stream, a);
-  else
-    hipLaunchKernelGGL(combine_kernel<kUnroll>, grid, dim3(64 * kCombineWaves), 0, stream, a);
+  auto go = [&](auto e) {
+    using E = decltype(e);
+    if (few)
+      hipLaunchKernelGGL((combine_kernel<kUnrollFew, E>), grid, dim3(64 * kCombineWaves), 0, stream, a);
+    else
+      hipLaunchKernelGGL((combine_kernel<kUnroll, E>), grid, dim3(64 * kCombineWaves), 0, stream, a);
+  };
+  if (a.f16) go(F16{});
+  else go(Bf16{});
   return hipGetLastError();
 }
 

@@ -7,7 +7,7 @@ namespace mla {
 #define MLA_DECODE_PARAMS                                                                   \
   const uint16_t* __restrict__, const uint16_t* __restrict__, const int32_t* __restrict__,  \
       const int32_t* __restrict__, const int32_t* __restrict__, uint16_t* __restrict__,      \
-      float* __restrict__, float* __restrict__, float* __restrict__, DecodeArgs
+      float* __restrict__, uint16_t* __restrict__, float* __restrict__, DecodeArgs
 #define MLA_DECODE_INSTANCES(E)                                                      \
   template __global__ void decode_kernel<16, 1, 4, false, E>(MLA_DECODE_PARAMS);   \
   template __global__ void decode_kernel<16, 2, 2, false, E>(MLA_DECODE_PARAMS);   \

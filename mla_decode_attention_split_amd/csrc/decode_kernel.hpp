@@ -8,7 +8,7 @@
 // rows (Shared-KV); pages of 64 tokens are found through block_table
 // (ygpos news: paged cache with block size 64, BF16).  Each workgroup handles
 // one part of the split-KV partition (pieces of one or more sequences) for one
-// tile of query rows; a sequence cut into several pieces leaves fp32 partial
+// tile of query rows; a sequence cut into several pieces leaves 16-bit partial
 // outputs plus their log-sum-exp for the combine kernel (section 4, merge of
 // partial outputs).
 //
@@ -273,7 +273,7 @@ __global__ __launch_bounds__(64 * RG * DG, 1) void decode_kernel(
     const uint16_t* __restrict__ q_ptr, const uint16_t* __restrict__ kv_ptr,
     const int32_t* __restrict__ block_table, const int32_t* __restrict__ seqlens,
     const int32_t* __restrict__ meta, uint16_t* __restrict__ out, float* __restrict__ lse,
-    float* __restrict__ o_part, float* __restrict__ lse_part, DecodeArgs a) {
+    uint16_t* __restrict__ o_part, float* __restrict__ lse_part, DecodeArgs a) {
   using T = Tile<R, RG, DG>;
   constexpr int NW = T::NW, BM = T::BM, LPW = T::LPW, KS_W = T::KS_W, KB_W = T::KB_W;
   constexpr int NT = T::NT, OREGS = T::OREGS, NQ = T::NQ;
@@ -621,7 +621,7 @@ __global__ __launch_bounds__(64 * RG * DG, 1) void decode_kernel(
   const int q_row0 = (rg * R) % kStage;
 
   // Write the normalised output of one piece (scaled by `scale`): bf16 out and
-  // lse for a whole sequence, else fp32 partials for the combine.
+  // lse for a whole sequence, else 16-bit partials (and an fp32 lse) for the combine.
   // WIDE tiles read their AGPR tiles one at a time (a fence per tile keeps
   // the compiler from moving all 256 values to VGPRs at once).
   auto write_piece = [&](OAcc* oo, float scale, bool whole_, long long row, float lse_v) {
@@ -654,16 +654,21 @@ __global__ __launch_bounds__(64 * RG * DG, 1) void decode_kernel(
         }
       }
     } else {
+      // The partial row is stored in the 16-bit element type of the inputs:
+      // it is a convex combination of the sequence's value rows, so it is in
+      // that type's range, and its rounding is of the size of the final
+      // output's.  The combine adds the pieces in fp32.
       if (lse_writer) lse_part[row] = lse_v;
-      float* prow = o_part + row * kValueDim;
+      uint16_t* prow = o_part + row * kValueDim;
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
         tile_fence(nt);
 #pragma unroll
         for (int qd = 0; qd < QUADS; ++qd) {
-          *reinterpret_cast<float4*>(prow + dim_of(nt, qd)) =
-              make_float4(oo[nt][4 * qd + 0] * scale, oo[nt][4 * qd + 1] * scale,
-                          oo[nt][4 * qd + 2] * scale, oo[nt][4 * qd + 3] * scale);
+          uint2 pk;
+          pk.x = E::pack(oo[nt][4 * qd + 0] * scale, oo[nt][4 * qd + 1] * scale);
+          pk.y = E::pack(oo[nt][4 * qd + 2] * scale, oo[nt][4 * qd + 3] * scale);
+          *reinterpret_cast<uint2*>(prow + dim_of(nt, qd)) = pk;
         }
       }
     }
@@ -953,12 +958,82 @@ __global__ __launch_bounds__(64 * RG * DG, 1) void decode_kernel(
     constexpr int W_WA = 30;                   // score MFMAs before the first P V MFMA
     constexpr int W_NQR = W_NK - W_WA;
     constexpr int W_NSTEP = W_NK + W_NV;
+    // WIDE softmax of the previous stage's scores, spread over the first
+    // W_WA score MFMAs with at most four VALU instructions after each (a
+    // wave hides about that many under one MFMA; a whole slice of dependent
+    // instructions after a single MFMA stalls the issue of the next one).
+    // Every instruction's inputs come from an earlier step, except within
+    // the max tree:
+    //   steps 0-3  row max (a max3 tree), the cross-lane max, the scale;
+    //   steps 4-6  the rescale decision, alpha, the running max and sums;
+    //   steps 8-27 element i: exponent fma at step 8 + i, exp2 at 9 + i,
+    //              fp32 sum (two alternating partial sums) at 10 + i; pair
+    //              k = (2k, 2k + 1) rounded to the MFMA type at 11 + 2k and
+    //              added to the rounded-weight sum (two partial sums) at
+    //              12 + 2k;
+    //   step 27    the running sums.
+    // The rescale of O, when the running max rises, follows at step 7.
+    struct WSoft {
+      float m[5], ma, mb, mx, mn, al, th;
+      bool rs;
+      float f[SREGS], e[SREGS];
+      float s[2], r[2];
+      uint32_t pw[SREGS / 2];
+    };
+    constexpr int WS_LAST = 27;
+    auto wide_soft = [&](auto gc, const float* x, WSoft& q) {
+      constexpr int g = decltype(gc)::value;
+      if constexpr (g == 0) {
+        q.m[0] = fmaxf(fmaxf(x[0], x[1]), x[2]);
+        q.m[1] = fmaxf(fmaxf(x[3], x[4]), x[5]);
+        q.m[2] = fmaxf(fmaxf(x[6], x[7]), x[8]);
+        q.th = m_run + kTau;
+      } else if constexpr (g == 1) {
+        q.m[3] = fmaxf(fmaxf(x[9], x[10]), x[11]);
+        q.m[4] = fmaxf(fmaxf(x[12], x[13]), x[14]);
+        q.ma = fmaxf(fmaxf(q.m[0], q.m[1]), q.m[2]);
+      } else if constexpr (g == 2) {
+        q.mb = fmaxf(fmaxf(q.m[3], q.m[4]), x[15]);
+      } else if constexpr (g == 3) {
+        q.mx = max_xor32(fmaxf(q.ma, q.mb)) * a.scale_log2;  // the max of the scaled scores (scale > 0)
+      } else if constexpr (g == 4) {
+        q.rs = __any(q.mx > q.th);
+        q.mn = fmaxf(m_run, q.mx);
+      } else if constexpr (g == 5) {
+        q.al = q.rs ? fast_exp2(m_run - q.mn) : 1.f;
+      } else if constexpr (g == 6) {
+        m_run = q.rs ? q.mn : m_run;
+        l_run *= q.al;
+        lr_run *= q.al;
+      } else if constexpr (g >= 8 && g <= WS_LAST) {
+        constexpr int i = g - 8;
+        if constexpr (i <= SREGS - 1) q.f[i] = __builtin_fmaf(x[i], a.scale_log2, -m_run);
+        if constexpr (i >= 1 && i <= SREGS) q.e[i - 1] = fast_exp2(q.f[i - 1]);
+        if constexpr (i >= 2 && i <= SREGS + 1) {
+          if constexpr (i - 2 < 2) q.s[(i - 2) & 1] = q.e[i - 2];
+          else q.s[(i - 2) & 1] += q.e[i - 2];
+        }
+        if constexpr (i >= 3 && (i - 3) % 2 == 0 && (i - 3) / 2 < SREGS / 2) {
+          constexpr int k = (i - 3) / 2;
+          q.pw[k] = E::pack(q.e[2 * k], q.e[2 * k + 1]);
+        }
+        if constexpr (i >= 4 && (i - 4) % 2 == 0 && (i - 4) / 2 < SREGS / 2) {
+          constexpr int k = (i - 4) / 2;
+          q.r[k & 1] = E::dot2(q.pw[k], E::kOnePair, k < 2 ? 0.f : q.r[k & 1]);
+        }
+        if constexpr (g == WS_LAST) {
+          l_run += q.s[0] + q.s[1];
+          lr_run += q.r[0] + q.r[1];
+        }
+      }
+    };
     auto wide_step = [&](auto hp, auto hc, const char MLA_LDS* __restrict__ rd,
                          const char MLA_LDS* __restrict__ prev, int s) {
       if constexpr (T::WIDE) {
         constexpr bool HP = decltype(hp)::value, HC = decltype(hc)::value;
         constexpr int QD = MLA_QD32;  // fragment queue depth
-        static_assert(W_WA >= kSoftSlices && W_WA < W_NK, "softmax slices fit before the P V MFMAs");
+        static_assert(W_WA > WS_LAST && W_WA < W_NK, "the softmax fits before the P V MFMAs");
+        static_assert(SREGS == 16 && 8 + SREGS + 3 <= WS_LAST, "the softmax steps cover every score");
         float x[SREGS];
         if constexpr (HP) {
 #pragma unroll
@@ -966,6 +1041,7 @@ __global__ __launch_bounds__(64 * RG * DG, 1) void decode_kernel(
           prep(x, s - 1);
         }
         SoftState ss;
+        WSoft ws;
         if constexpr (HC) {
           constexpr int NS = HP ? W_NSTEP : W_NK;  // without a previous stage: scores only
           // step g: a score MFMA (k-step qk(g)) or P V MFMA pv(g)
@@ -997,30 +1073,24 @@ __global__ __launch_bounds__(64 * RG * DG, 1) void decode_kernel(
             }
             if constexpr (g + QD < NS) fq[g % QD] = read_frag(std::integral_constant<int, g + QD>{});
             if constexpr (HP) {
-              // the softmax slices spread over the first W_WA - 2 score MFMAs
-              constexpr int SPAN = W_WA - 2;
-              if constexpr ((g * kSoftSlices) % SPAN < kSoftSlices && (g * kSoftSlices) / SPAN < kSoftSlices)
-                soft_slice(x, ss, (g * kSoftSlices) / SPAN);
-              // Right after the slice that decides it (before the
-              // exponentials, which then stay between the score MFMAs
-              // instead of being moved past the branch): rescale O if the
-              // running max rose (O is still zero before the first stage).
-              constexpr int G_RS = (2 * SPAN + kSoftSlices - 1) / kSoftSlices + 1;
-              if constexpr (g == G_RS) {
-                if (ss.rescale && s - 1 > 0) {
+              if constexpr (g <= WS_LAST) wide_soft(gc, x, ws);
+              // Right after the running max is decided: rescale O if it rose
+              // (O is still zero before the first stage of a piece).
+              if constexpr (g == 7) {
+                if (ws.rs && s - 1 > 0) {
 #pragma unroll
                   for (int nt = 0; nt < NT; ++nt) {
                     if (nt == 0) agpr_fence_one<18>(o[nt]);
                     else agpr_fence_one<0>(o[nt]);
-                    acc_scale<OREGS>(o[nt], ss.alpha);
+                    acc_scale<OREGS>(o[nt], ws.al);
                     if (nt == NT - 1) agpr_fence_one<2>(o[nt]);
                     else agpr_fence_one<0>(o[nt]);
                   }
                 }
               }
               if constexpr (g == W_WA - 1) {  // the softmax is complete: P as MFMA operands
-                pb[0] = __builtin_bit_cast(i16x8, i32x4{(int)ss.pw[0], (int)ss.pw[1], (int)ss.pw[2], (int)ss.pw[3]});
-                pb[1] = __builtin_bit_cast(i16x8, i32x4{(int)ss.pw[4], (int)ss.pw[5], (int)ss.pw[6], (int)ss.pw[7]});
+                pb[0] = __builtin_bit_cast(i16x8, i32x4{(int)ws.pw[0], (int)ws.pw[1], (int)ws.pw[2], (int)ws.pw[3]});
+                pb[1] = __builtin_bit_cast(i16x8, i32x4{(int)ws.pw[4], (int)ws.pw[5], (int)ws.pw[6], (int)ws.pw[7]});
               }
             }
             __builtin_amdgcn_sched_barrier(0);

@@ -10,7 +10,7 @@ namespace mla {
 #define MLA_WIDE_PARAMS                                                                     \
   const uint16_t* __restrict__, const uint16_t* __restrict__, const int32_t* __restrict__,  \
       const int32_t* __restrict__, const int32_t* __restrict__, uint16_t* __restrict__,      \
-      float* __restrict__, float* __restrict__, float* __restrict__, DecodeArgs
+      float* __restrict__, uint16_t* __restrict__, float* __restrict__, DecodeArgs
 template __global__ void decode_kernel<32, 4, 1, false, Bf16>(MLA_WIDE_PARAMS);
 template __global__ void decode_kernel<32, 4, 1, false, F16>(MLA_WIDE_PARAMS);
 

@@ -17,7 +17,7 @@ struct DecodeArgs {
   const int32_t* num_splits;  // [batch + 1]
   uint16_t* out;              // q's type, [batch, s_q, h_q, 512]
   float* lse;                 // [batch, s_q, h_q]
-  float* o_part;              // [max_pieces, h_kv, M, 512]
+  uint16_t* o_part;           // [max_pieces, h_kv, M, 512] in the element type of q
   float* lse_part;            // [max_pieces, h_kv, M]
   int batch, s_q, h_q, h_kv, M, max_blocks, num_parts, m_tiles;
   int num_pages;              // pages in blocked_k: a table entry outside [0, num_pages) reads zeros
@@ -29,7 +29,7 @@ struct DecodeArgs {
 
 struct CombineArgs {
   const int32_t* num_splits;
-  const float* o_part;
+  const uint16_t* o_part;     // 16-bit partial rows (element type of out)
   const float* lse_part;
   uint16_t* out;
   float* lse;

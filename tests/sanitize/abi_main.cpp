@@ -81,7 +81,7 @@ int main() {
   EXPECT_EQ(mla_tile_shape(0, 1, &tr, &mt, &fc), MLA_ERR_UNSUPPORTED);
   EXPECT_EQ(mla_tile_shape(16, 0, nullptr, nullptr, nullptr), MLA_ERR_INVALID_ARG);
   EXPECT_EQ(mla_workspace_bytes(32, 16, 1, 256, 512),
-            (32 + 256) * 16 * 2048 + ((32 + 256) * 16 * 4 + 255) / 256 * 256);
+            (32 + 256) * 16 * 1024 + ((32 + 256) * 16 * 4 + 255) / 256 * 256);
   EXPECT_EQ(mla_workspace_bytes(MLA_MAX_BATCH, MLA_MAX_ROWS, 1, MLA_MAX_PARTS, 512) > 0, 1);
   EXPECT_EQ(mla_workspace_bytes(0, 16, 1, 256, 512), 0);
   EXPECT_EQ(mla_workspace_bytes(4, 16, 1, 256, 511), 0);

@@ -71,10 +71,10 @@ def test_status_strings():
 
 def test_workspace_size_formula():
     lib = mla._load()
-    # (batch + num_parts) pieces x h_kv x rows x (512 fp32 + one fp32 lse, 256-B aligned)
+    # (batch + num_parts) pieces x h_kv x rows x (512 16-bit values + one fp32 lse, 256-B aligned)
     n = lib.mla_workspace_bytes(32, 16, 1, 256, 512)
     rows = (32 + 256) * 16
-    assert n == rows * 512 * 4 + ((rows * 4 + 255) // 256) * 256
+    assert n == rows * 512 * 2 + ((rows * 4 + 255) // 256) * 256
     assert lib.mla_workspace_bytes(0, 16, 1, 256, 512) == 0
     assert lib.mla_workspace_bytes(4, 0, 1, 256, 512) == 0
     assert lib.mla_workspace_bytes(4, 16, 1, 0, 512) == 0
