@@ -620,58 +620,105 @@ __global__ __launch_bounds__(64 * RG * DG, 1) void decode_kernel(
   const int q_stage = (rg * R) / kStage;
   const int q_row0 = (rg * R) % kStage;
 
-  // Write the normalised output of one piece (scaled by `scale`): bf16 out and
-  // lse for a whole sequence, else 16-bit partials (and an fp32 lse) for the combine.
+  // Write the normalised output of one piece (scaled by `scale`): out and lse
+  // for a whole sequence, else 16-bit partials (and an fp32 lse) for the
+  // combine.  Rows leave through LDS: in the MFMA layout a lane holds a few
+  // 8-byte pieces of one row, and a store of that layout touches 16-32 rows,
+  // which the store path serves at a fraction of its contiguous rate.  So
+  // every wave first writes its values into the two ring slots the piece's
+  // last stages used (free once every wave is past them; the two positions
+  // in flight use the other two slots), rows at a padded pitch, and the
+  // workgroup then stores whole rows, 16 contiguous bytes per lane.  The
+  // 128-row tile does this in two rounds, one per half of the value dims
+  // (a 512-byte half row per 32 lanes).
   // WIDE tiles read their AGPR tiles one at a time (a fence per tile keeps
   // the compiler from moving all 256 values to VGPRs at once).
-  auto write_piece = [&](OAcc* oo, float scale, bool whole_, long long row, float lse_v) {
+  constexpr int ROUNDS = BM > 64 ? 2 : 1;
+  constexpr int DR = kValueDim / ROUNDS;                   // value dims per round
+  constexpr int kStagePitch = DR * 2 + 16;                 // bytes per staged row
+  constexpr int LPR = DR * 2 / 16;                         // lanes per staged row
+  constexpr int RPI = 64 / LPR;                            // rows per store instruction
+  constexpr int kRowsPerSlot = kStageBytes / kStagePitch / RPI * RPI;  // whole store groups
+  static_assert(BM <= 2 * kRowsPerSlot, "the staged rows fit in two ring slots");
+  static_assert(ROUNDS == 1 || (T::WIDE && NT % ROUNDS == 0), "two rounds: 128-row tile");
+  static_assert(BM % (RPI * NW) == 0, "staged rows split evenly over the waves");
+  auto write_piece = [&](OAcc* oo, float scale, bool whole_, long long row, float lse_v, int b_,
+                         int slot_) {
     auto tile_fence = [&](int nt) {
       if constexpr (T::WIDE) {
-        if (nt == 0) agpr_fence_one<18>(oo[nt]);
+        if (nt % (NT / ROUNDS) == 0) agpr_fence_one<18>(oo[nt]);
         else agpr_fence_one<0>(oo[nt]);
       }
     };
-    if (my_row >= M) return;
-    const bool lse_writer = dg == 0 && lane < R;
+    const bool lse_writer = dg == 0 && lane < R && my_row < M;
+    if (lse_writer) {
+      if (whole_) lse[row] = lse_v;
+      else lse_part[row] = lse_v;
+    }
     // dims held by this lane: 4 consecutive dims per group of 4 accumulators
     auto dim_of = [&](int nt, int qd) {
       const int nb = dg * NT + nt;
       return R == 32 ? 32 * nb + 8 * qd + 4 * (lane >> 5) : 16 * nb + 4 * (lane >> 4);
     };
     constexpr int QUADS = OREGS / 4;
-    if (whole_) {
-      if (lse_writer) lse[row] = lse_v;
-      uint16_t* orow = out + row * kValueDim;
+    char MLA_LDS* sA = slot_of(cstage - 2);
+    char MLA_LDS* sB = slot_of(cstage - 1);
+    auto srow = [&](int r) {
+      return r < kRowsPerSlot ? sA + r * kStagePitch : sB + (r - kRowsPerSlot) * kStagePitch;
+    };
+    // The tile's destination rows: those of a partial, and with one KV head
+    // those of out, are consecutive (tile row l at byte 1024 l of a buffer
+    // that ends at the tile's last valid row, so rows past M store nothing).
+    // With several KV heads a whole sequence's rows are found one by one.
+    const int valid_rows = M - m_lo < BM ? M - m_lo : BM;
+    const uint16_t* dbase = whole_ ? out + ((long long)b_ * a.s_q * a.h_q + m_lo) * kValueDim
+                                   : o_part + (((long long)slot_ * a.h_kv + g) * M + m_lo) * kValueDim;
+    const __amdgpu_buffer_rsrc_t drs = make_rsrc(dbase, valid_rows * kValueDim * 2);
+    // this lane's part of a store: row lane / LPR of the group, 16 bytes c
+    // (opaque to the compiler, which would otherwise compute every store's
+    // offset once, before the loop over pieces, and keep them all in
+    // registers)
+    const int c = lane % LPR;
+    unsigned lds_lane = (lane / LPR) * kStagePitch + 16 * c;
+    unsigned glb_lane = (lane / LPR) * kValueDim * 2 + 16 * c;
+    asm volatile("" : "+v"(lds_lane), "+v"(glb_lane));
+    static_for<ROUNDS>([&](auto rc) {
+      constexpr int rd = decltype(rc)::value;
+      // every wave is past the slots (the last stages' reads, or the
+      // previous round's row stores)
+      block_barrier();
+      char MLA_LDS* p = srow(rg * R + lr) - 2 * rd * DR;
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
+      for (int nt = rd * NT / ROUNDS; nt < (rd + 1) * NT / ROUNDS; ++nt) {
         tile_fence(nt);
 #pragma unroll
         for (int qd = 0; qd < QUADS; ++qd) {
-          uint2 pk;
-          pk.x = E::pack(oo[nt][4 * qd + 0] * scale, oo[nt][4 * qd + 1] * scale);
-          pk.y = E::pack(oo[nt][4 * qd + 2] * scale, oo[nt][4 * qd + 3] * scale);
-          *reinterpret_cast<uint2*>(orow + dim_of(nt, qd)) = pk;
+          const i32x2 pk = {(int)E::pack(oo[nt][4 * qd + 0] * scale, oo[nt][4 * qd + 1] * scale),
+                            (int)E::pack(oo[nt][4 * qd + 2] * scale, oo[nt][4 * qd + 3] * scale)};
+          *reinterpret_cast<i32x2 MLA_LDS*>(p + 2 * dim_of(nt, qd)) = pk;
         }
       }
-    } else {
-      // The partial row is stored in the 16-bit element type of the inputs:
-      // it is a convex combination of the sequence's value rows, so it is in
-      // that type's range, and its rounding is of the size of the final
-      // output's.  The combine adds the pieces in fp32.
-      if (lse_writer) lse_part[row] = lse_v;
-      uint16_t* prow = o_part + row * kValueDim;
+      block_barrier();  // the round's rows are staged
+      // store instruction k of wave w: tile rows l0 = (w + k NW) RPI and on
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        tile_fence(nt);
-#pragma unroll
-        for (int qd = 0; qd < QUADS; ++qd) {
-          uint2 pk;
-          pk.x = E::pack(oo[nt][4 * qd + 0] * scale, oo[nt][4 * qd + 1] * scale);
-          pk.y = E::pack(oo[nt][4 * qd + 2] * scale, oo[nt][4 * qd + 3] * scale);
-          *reinterpret_cast<uint2*>(prow + dim_of(nt, qd)) = pk;
+      for (int k = 0; k < BM / (RPI * NW); ++k) {
+        const int l0 = (w + k * NW) * RPI;
+        const i32x4 v = *reinterpret_cast<const i32x4 MLA_LDS*>(srow(l0) + lds_lane);
+        if constexpr (QG) {
+          if (whole_) {  // rows of several KV heads: out row of query row m
+            const int m = m_lo + l0 + lane / LPR;
+            const int t = m / hpg;
+            const int h = g * hpg + (m - t * hpg);
+            if (m < M)
+              *reinterpret_cast<i32x4*>(out + (((long long)b_ * a.s_q + t) * a.h_q + h) * kValueDim +
+                                        rd * DR + 8 * c) = v;
+            continue;
+          }
         }
+        // (the whole offset goes in the checked per-lane offset)
+        __builtin_amdgcn_raw_buffer_store_b128(v, drs, glb_lane + (unsigned)(l0 * kValueDim * 2 + rd * DR * 2), 0, 0);
       }
-    }
+    });
   };
   // 16-row tiles hold the normalised output of the first piece that is not
   // the part's last in registers and write it after the last piece: stores
@@ -684,6 +731,7 @@ __global__ __launch_bounds__(64 * RG * DG, 1) void decode_kernel(
   bool def_whole = false;
   long long def_row = 0;
   float def_lse = 0.f;
+  int def_b = 0, def_slot = 0;
 
   for (int j = 0; j < npieces; ++j) {
     const int b = bb + j;
@@ -1188,13 +1236,15 @@ __global__ __launch_bounds__(64 * RG * DG, 1) void decode_kernel(
         def_whole = whole;
         def_row = row;
         def_lse = lse_row;
+        def_b = b;
+        def_slot = slot;
         continue;
       }
     }
-    write_piece(o, inv, whole, row, lse_row);
+    write_piece(o, inv, whole, row, lse_row, b, slot);
   }
   if constexpr (DEFER) {
-    if (def_pending) write_piece(o_def, 1.f, def_whole, def_row, def_lse);
+    if (def_pending) write_piece(o_def, 1.f, def_whole, def_row, def_lse, def_b, def_slot);
   }
   // Out-of-range loads past the end of the stream may still be in flight:
   // they must land before the workgroup's LDS is released.
