@@ -255,6 +255,9 @@ struct Tile {
   static constexpr int QREG_STEPS = KS_W - QR_STEPS;     // Q^T k-steps held in registers
   static constexpr int QR_BYTES = NW * QR_STEPS * 1024;
   static constexpr int NQ = (BM + kStage - 1) / kStage;  // query stages per piece
+  // Query stages in the ring: WIDE tiles load Q^T straight into their
+  // registers (and the rope steps into LDS) instead.
+  static constexpr int NQS = WIDE ? 0 : NQ;
   static constexpr int QK_MFMA = KS_W * KB_W;
   static constexpr int PV_MFMA = R == 32 ? 2 * NT : NT;
   static constexpr int NSLOT = QK_MFMA + PV_MFMA;        // points where loads are issued
@@ -276,7 +279,7 @@ __global__ __launch_bounds__(64 * RG * DG, 1) void decode_kernel(
     uint16_t* __restrict__ o_part, float* __restrict__ lse_part, DecodeArgs a) {
   using T = Tile<R, RG, DG>;
   constexpr int NW = T::NW, BM = T::BM, LPW = T::LPW, KS_W = T::KS_W, KB_W = T::KB_W;
-  constexpr int NT = T::NT, OREGS = T::OREGS, NQ = T::NQ;
+  constexpr int NT = T::NT, OREGS = T::OREGS;
   using OAcc = typename std::conditional<R == 32, f32x16, f32x4>::type;
   constexpr int SREGS = R == 32 ? 16 : 8;  // scores per lane per stage
 
@@ -456,10 +459,10 @@ __global__ __launch_bounds__(64 * RG * DG, 1) void decode_kernel(
 
   // ---- stage stream -----------------------------------------------------------
   // For every non-empty piece: NQ query stages (32 rows of the tile each, same
-  // swizzled row layout as the keys), then the piece's key stages.  Stream
-  // position c uses ring slot c % 4; position c + 2 is loaded while
-  // position c is computed.  Past the end of the stream the loads are out of
-  // range.
+  // swizzled row layout as the keys; none in WIDE tiles), then the piece's
+  // key stages.  Stream position c uses ring slot c % 4; position c + 2 is
+  // loaded while position c is computed.  Past the end of the stream the
+  // loads are out of range.
   // Cursor of the stream: piece lj, query stage lq, key token ltok (end lhi),
   // and the next key stage's page-list position lpos and page half lhalf.
   int lj = 0, lq = 0, ltok = tb, lhi = (bb == be) ? te : n_first;
@@ -566,7 +569,7 @@ __global__ __launch_bounds__(64 * RG * DG, 1) void decode_kernel(
     pend_dst = wr + w * 1024;
     pend_q = false;
     pend_nt = false;
-    if (lvalid && lq >= NQ) {
+    if (lvalid && lq >= T::NQS) {
       pend_nt = nt_kv;
       int page;
       if (use_list) page = readlane(LIST_HALVES == 1 || lpos < 64 ? v_page[0] : v_page[LIST_HALVES - 1], lpos & 63);
@@ -602,6 +605,38 @@ __global__ __launch_bounds__(64 * RG * DG, 1) void decode_kernel(
       pend = make_rsrc(kv_bytes, 0);
     }
   };
+  // Q^T fragments of the current piece (B operands of the score MFMAs).
+  // WIDE tiles load them straight from q: lane l's k-step ks is the 16 bytes
+  // of query row w R + l % 32 at dims 16 ks + 8 (l / 32), i.e. one 16-byte
+  // load per k-step into the registers; the rope k-steps go into the wave's
+  // LDS area by DMA, in the layout they are read in (lane l at 16 l).  Rows
+  // past the tile's last valid row are out of the buffer's range and load
+  // zeros.  The next piece's Q^T is loaded right after the current piece's
+  // last score MFMAs, so its latency hides behind the last P V MFMAs and the
+  // epilogue, and the prefetched stages of the ring are key stages only.
+  i16x8 qf[T::QREG_STEPS];
+  int q_piece = -1;  // piece whose Q^T is in qf (or in flight)
+  const unsigned q_lane = (unsigned)((w * R + lr) * kRowBytes + 16 * (lane >> 5));
+  char MLA_LDS* qr_wave = xch0 + T::XCH_BUFS * T::XCH_ONE + w * T::QR_STEPS * 1024;  // wave-uniform
+  auto load_q = [&](int jn) {
+    if constexpr (T::WIDE) {
+      const char* qb = reinterpret_cast<const char*>(q_ptr) +
+                       ((long long)(bb + jn) * a.s_q * a.h_q + m_lo) * kRowBytes;
+      const __amdgpu_buffer_rsrc_t qrs = make_rsrc(qb, (m_hi - m_lo) * kRowBytes);
+      // (opaque, so that the step offsets go into the loads' offset field
+      // instead of 36 registers computed once before the loop over pieces)
+      unsigned ql = q_lane;
+      asm volatile("" : "+v"(ql));
+#pragma unroll
+      for (int ks = 0; ks < T::QREG_STEPS; ++ks)
+        qf[ks] = __builtin_bit_cast(i16x8, __builtin_amdgcn_raw_buffer_load_b128(qrs, ql + 32 * ks, 0, 0));
+#pragma unroll
+      for (int j = 0; j < T::QR_STEPS; ++j)
+        load_lds16_asm<false>(qrs, ql + 32 * (T::QREG_STEPS + j), qr_wave + 1024 * j);
+      q_piece = jn;
+    }
+  };
+  if (T::WIDE && lvalid) load_q(lj);  // the first piece with keys
   plan(lds);
   fire_all();
   plan(lds + kStageBytes);
@@ -751,7 +786,6 @@ __global__ __launch_bounds__(64 * RG * DG, 1) void decode_kernel(
     for (int nt = 0; nt < NT; ++nt) o[nt] = OAcc{};
     if constexpr (T::WIDE) agpr_fence_write(o);
     float m_run = kMinit, l_run = 0.f, lr_run = 0.f;
-    i16x8 qf[T::QREG_STEPS];
 
     // Mask the raw scores of key stage sp (keys past the end, or past the
     // row's causal limit).  The scale (positive) is applied later: to the
@@ -1154,13 +1188,16 @@ __global__ __launch_bounds__(64 * RG * DG, 1) void decode_kernel(
 
     if (nst > 0) {
       // WIDE: a vector-memory wait the compiler can see (a builtin, not asm)
-      // at the start of each piece, while only the piece's first query
-      // stages are in flight.  Register spill stores made outside the stage
-      // loop are then known to be complete, and the compiler puts no wait of
-      // its own into the stage loop (there it drained the prefetched stages
-      // in every iteration).
-      if constexpr (T::WIDE) __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-      for (int jq = 0; jq < NQ; ++jq, ++cstage) {
+      // at the start of each piece, while only the piece's Q^T and first two
+      // key stages are in flight (and the previous piece's stores draining).
+      // The Q^T registers are then known to be loaded, and the compiler puts
+      // no wait of its own into the stage loop (there it drained the
+      // prefetched stages in every iteration).
+      if constexpr (T::WIDE) {
+        if (q_piece != j) load_q(j);
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+      }
+      for (int jq = 0; jq < T::NQS; ++jq, ++cstage) {
         stage_ready();
         [&](const char MLA_LDS* __restrict__ rd, char MLA_LDS* __restrict__ wr) {
           plan(wr);
@@ -1190,6 +1227,8 @@ __global__ __launch_bounds__(64 * RG * DG, 1) void decode_kernel(
           fire_all();
           wide_step(Tr{}, Tr{}, slot_of(cstage), slot_of(cstage - 1), s);
         }
+        // The score MFMAs of the piece are done: the next piece's Q^T.
+        if (j + 1 < npieces) load_q(j + 1);
         // drain: finish the last stage (its scores are in registers)
         wide_step(Tr{}, F{}, slot_of(cstage), slot_of(cstage - 1), nst);
       } else {
