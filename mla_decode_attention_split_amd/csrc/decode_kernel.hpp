@@ -13,19 +13,20 @@
 // partial outputs).
 //
 // Design (gfx950):
-//   * One workgroup per CU, 4 waves (one per SIMD).  The part's stages (query
-//     rows, then 32-key blocks, per piece) stream through a ring of 4 LDS
-//     slots of 36 KB with 16-byte buffer loads straight into LDS.  Every ring
-//     position is loaded with the same number of instructions per wave; lanes
-//     with nothing to load address past their buffer's range, which costs no
+//   * One workgroup per CU, 4 waves (one per SIMD).  The part's key stages
+//     (32-key blocks of its pieces) stream through a ring of 4 LDS slots of
+//     36 KB with 16-byte buffer loads straight into LDS.  Every ring position
+//     is loaded with the same number of instructions per wave; lanes with
+//     nothing to load address past their buffer's range, which costs no
 //     memory traffic, so the per-stage waits are exact constants.
 //   * The prologue needs one memory trip after the part's metadata record:
 //     the record carries the lengths and partial slots of the part's first
 //     and last sequence, and the page indices of the part are loaded into
-//     registers (lane i holds entry i) while the query stage is already in
-//     flight.
+//     registers (lane i holds entry i) while the first piece's query rows are
+//     already in flight.
 //   * Scores are computed transposed, S^T = K Q^T, with K from LDS (A
-//     operand) and Q^T resident in registers (B operand); the MFMA result is
+//     operand) and Q^T loaded from q straight into registers, where it stays
+//     for the piece (B operand); the MFMA result is
 //     already laid out as the B operand P^T of O^T = V^T P^T.  V^T comes from
 //     LDS through transposed 8-byte reads (ds_read_b64_tr_b16).
 //   * Tiles of up to 64 rows (split-K): each wave owns R query rows (R = 16
@@ -254,10 +255,14 @@ struct Tile {
   static constexpr int QR_STEPS = WIDE ? 4 : 0;
   static constexpr int QREG_STEPS = KS_W - QR_STEPS;     // Q^T k-steps held in registers
   static constexpr int QR_BYTES = NW * QR_STEPS * 1024;
+  // Query rows (Q^T): the 16-row and 128-row tiles load them from q straight
+  // into registers (DQ).  The 64-row tile streams them through the ring as
+  // NQS query stages per piece instead: a 32-row wave's direct loads touch
+  // 32 rows of 32 bytes per instruction, and with 18 of them per wave in
+  // each of its four waves this measured slower than two ring stages.
+  static constexpr bool DQ = WIDE || R == 16;
   static constexpr int NQ = (BM + kStage - 1) / kStage;  // query stages per piece
-  // Query stages in the ring: WIDE tiles load Q^T straight into their
-  // registers (and the rope steps into LDS) instead.
-  static constexpr int NQS = WIDE ? 0 : NQ;
+  static constexpr int NQS = DQ ? 0 : NQ;
   static constexpr int QK_MFMA = KS_W * KB_W;
   static constexpr int PV_MFMA = R == 32 ? 2 * NT : NT;
   static constexpr int NSLOT = QK_MFMA + PV_MFMA;        // points where loads are issued
@@ -271,7 +276,11 @@ struct Tile {
   static_assert(RING_BYTES + XCH_BUFS * XCH_ONE + QR_BYTES <= 163840, "LDS capacity");
 };
 
-template <int R, int RG, int DG, bool QG, typename E>
+// NTK: the key stages load non-temporally (the launch sets it when no other
+// row tile of a part reads the same pages).  It is a template parameter so
+// that every ring position is one straight run of loads, which the
+// compiler's count of outstanding loads follows exactly.
+template <int R, int RG, int DG, bool QG, bool NTK, typename E>
 __global__ __launch_bounds__(64 * RG * DG, 1) void decode_kernel(
     const uint16_t* __restrict__ q_ptr, const uint16_t* __restrict__ kv_ptr,
     const int32_t* __restrict__ block_table, const int32_t* __restrict__ seqlens,
@@ -386,6 +395,10 @@ __global__ __launch_bounds__(64 * RG * DG, 1) void decode_kernel(
       }
       if (idx >= 0) v_page[half] = block_table[idx];
     }
+    // The first position needs the list: wait for it here, where the
+    // compiler sees it (else it finds the list possibly in flight wherever
+    // the stream reads it, and drains the prefetched stages there).
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
   }
 
   // ---- lane constants --------------------------------------------------------
@@ -458,11 +471,11 @@ __global__ __launch_bounds__(64 * RG * DG, 1) void decode_kernel(
   auto key_reg = [](int i) -> int { return R == 32 ? 8 * (i >> 2) + (i & 3) : 16 * (i >> 2) + (i & 3); };
 
   // ---- stage stream -----------------------------------------------------------
-  // For every non-empty piece: NQ query stages (32 rows of the tile each, same
-  // swizzled row layout as the keys; none in WIDE tiles), then the piece's
-  // key stages.  Stream position c uses ring slot c % 4; position c + 2 is
-  // loaded while position c is computed.  Past the end of the stream the
-  // loads are out of range.
+  // For every non-empty piece: NQS query stages (32 rows of the tile each,
+  // same swizzled row layout as the keys; none in DQ tiles), then the
+  // piece's key stages.  Stream position c uses ring slot c % 4; position
+  // c + 2 is loaded while position c is computed.  Past the end of the
+  // stream the loads are out of range.
   // Cursor of the stream: piece lj, query stage lq, key token ltok (end lhi),
   // and the next key stage's page-list position lpos and page half lhalf.
   int lj = 0, lq = 0, ltok = tb, lhi = (bb == be) ? te : n_first;
@@ -498,9 +511,12 @@ __global__ __launch_bounds__(64 * RG * DG, 1) void decode_kernel(
   // buffer that starts at the stage's first row and ends at the tile's last
   // valid row.  Otherwise (QG) every lane's offset is computed.
   bool pend_q = false;
-  bool pend_nt = false;  // the pending position's loads are non-temporal
   static_assert(!(QG && T::WIDE), "the WIDE tile serves one KV head");
-  unsigned qoff[QG ? LPW : 1];
+  // (query stages use the default cache policy: the pieces of a sequence
+  // split over many parts all read its query rows)
+  static_assert(T::NQS == 0 || !NTK, "tiles with query stages keep the default policy");
+  constexpr bool QOFF = QG && T::NQS > 0;
+  unsigned qoff[QOFF ? LPW : 1];
   // Query row m of the KV head is token m / hpg, head g hpg + m % hpg; the
   // quotient comes from a float reciprocal (m is below 2^13, so the product
   // is off by far less than one and truncation errs by at most one) and one
@@ -524,29 +540,20 @@ __global__ __launch_bounds__(64 * RG * DG, 1) void decode_kernel(
     return m < m_hi ? (unsigned)((t * q_hq + g * hpg + h) * kRowBytes + phys_chunk<R>(row, pc) * 16)
                     : kOutOfRange;
   };
-  // Key stages load non-temporally unless other row tiles of the part read
-  // the same pages; query stages never do (the pieces of a sequence split
-  // over many parts all read its query rows).  The 4-wave 64-row tile (two
-  // row groups of 32 rows) measured ~0.7 us slower with it on the ragged
-  // batch and keeps the default policy.
-  const bool nt_kv = a.m_tiles == 1 && (T::WIDE || !(R == 32 && NW == 4));
-  auto fire = [&](int k) {
-    if constexpr (QG) load_lds16(pend, pend_q ? qoff[k] : loff[k], pend_dst + k * NW * 1024, pend_nt);
-    else load_lds16(pend, loff[k], pend_dst + k * NW * 1024, pend_nt);
+  // (positions past the end of the stream load nothing, so the cache policy
+  // of their loads does not matter)
+  auto voff_of = [&](int k) -> unsigned {
+    if constexpr (QOFF) return pend_q ? qoff[k] : loff[k];
+    else return loff[k];
   };
-  // All LPW loads of the pending position, with one branch on the cache
-  // policy for the whole position.
+  auto fire = [&](int k) { load_lds16(pend, voff_of(k), pend_dst + k * NW * 1024, NTK); };
+  // All LPW loads of the pending position.
   auto fire_all = [&]() {
-    auto fire_nt = [&](auto nt) {
 #pragma unroll
-      for (int k = 0; k < LPW; ++k) {
-        const unsigned vo = QG && pend_q ? qoff[QG ? k : 0] : loff[k];
-        if constexpr (T::WIDE) load_lds16_asm<decltype(nt)::value>(pend, vo, pend_dst + k * NW * 1024);
-        else load_lds16(pend, vo, pend_dst + k * NW * 1024, decltype(nt)::value);
-      }
-    };
-    if (pend_nt) fire_nt(std::true_type{});
-    else fire_nt(std::false_type{});
+    for (int k = 0; k < LPW; ++k) {
+      if constexpr (T::WIDE) load_lds16_asm<NTK>(pend, loff[k], pend_dst + k * NW * 1024);
+      else load_lds16(pend, voff_of(k), pend_dst + k * NW * 1024, NTK);
+    }
   };
   // issue point s of the stage's NSLOT points fires loads k with
   // k * NSLOT / LPW == s (resolved at compile time)
@@ -568,9 +575,7 @@ __global__ __launch_bounds__(64 * RG * DG, 1) void decode_kernel(
   auto plan = [&](char MLA_LDS* __restrict__ wr) {
     pend_dst = wr + w * 1024;
     pend_q = false;
-    pend_nt = false;
     if (lvalid && lq >= T::NQS) {
-      pend_nt = nt_kv;
       int page;
       if (use_list) page = readlane(LIST_HALVES == 1 || lpos < 64 ? v_page[0] : v_page[LIST_HALVES - 1], lpos & 63);
       else page = sload_i32(block_table + (long long)(bb + lj) * a.max_blocks + (ltok >> 6));
@@ -590,7 +595,7 @@ __global__ __launch_bounds__(64 * RG * DG, 1) void decode_kernel(
       const int b = bb + lj;
       const char* qseq = reinterpret_cast<const char*>(q_ptr) + (long long)b * a.s_q * a.h_q * kRowBytes;
       const int m0 = m_lo + kStage * lq;
-      if constexpr (QG) {
+      if constexpr (QOFF) {
         pend = make_rsrc(qseq, a.s_q * a.h_q * kRowBytes);
         pend_q = true;
 #pragma unroll
@@ -605,42 +610,58 @@ __global__ __launch_bounds__(64 * RG * DG, 1) void decode_kernel(
       pend = make_rsrc(kv_bytes, 0);
     }
   };
-  // Q^T fragments of the current piece (B operands of the score MFMAs).
-  // WIDE tiles load them straight from q: lane l's k-step ks is the 16 bytes
-  // of query row w R + l % 32 at dims 16 ks + 8 (l / 32), i.e. one 16-byte
-  // load per k-step into the registers; the rope k-steps go into the wave's
-  // LDS area by DMA, in the layout they are read in (lane l at 16 l).  Rows
-  // past the tile's last valid row are out of the buffer's range and load
-  // zeros.  The next piece's Q^T is loaded right after the current piece's
-  // last score MFMAs, so its latency hides behind the last P V MFMAs and the
-  // epilogue, and the prefetched stages of the ring are key stages only.
+  // Q^T fragments of the current piece (B operands of the score MFMAs).  DQ
+  // tiles load them straight from q into the registers: the wave's local k-step j is
+  // k-step ks = KSPLIT j + kh, and lane l's fragment of it is the 16 bytes of
+  // the lane's query row at dims 16 ks + 8 (l / 32) (R = 32) or
+  // 32 ks + 8 (l / 16) (R = 16), one 16-byte load per k-step.  WIDE tiles
+  // send their rope k-steps into the wave's LDS area by DMA instead, in the
+  // layout they are read in (lane l at 16 l).  Rows past the tile's last
+  // valid row load zeros (outside the buffer's range).  The next piece's Q^T
+  // is loaded right after the current piece's last score MFMAs, so its
+  // latency hides behind the last P V MFMAs and the epilogue, and the ring
+  // carries key stages only.
+  constexpr int QSTEP = (R == 32 ? 32 : 64) * T::KSPLIT;  // bytes between the wave's k-steps
   i16x8 qf[T::QREG_STEPS];
   int q_piece = -1;  // piece whose Q^T is in qf (or in flight)
-  const unsigned q_lane = (unsigned)((w * R + lr) * kRowBytes + 16 * (lane >> 5));
+  const unsigned q_sub = (unsigned)(R == 32 ? 16 * (lane >> 5) + 32 * kh : 16 * (lane >> 4) + 64 * kh);
+  // The lane's query row in the buffer of the piece's query rows: with one KV
+  // head the tile's rows are consecutive q rows (the buffer starts at the
+  // tile's first row); with several, row m is token m / hpg, head
+  // g hpg + m % hpg of the sequence.
+  const unsigned q_lane =
+      QG ? (my_row < M ? (unsigned)((q_t * a.h_q + q_h) * kRowBytes) + q_sub : kOutOfRange)
+         : (unsigned)((rg * R + lr) * kRowBytes) + q_sub;
   char MLA_LDS* qr_wave = xch0 + T::XCH_BUFS * T::XCH_ONE + w * T::QR_STEPS * 1024;  // wave-uniform
   auto load_q = [&](int jn) {
-    if constexpr (T::WIDE) {
-      const char* qb = reinterpret_cast<const char*>(q_ptr) +
-                       ((long long)(bb + jn) * a.s_q * a.h_q + m_lo) * kRowBytes;
-      const __amdgpu_buffer_rsrc_t qrs = make_rsrc(qb, (m_hi - m_lo) * kRowBytes);
-      // (opaque, so that the step offsets go into the loads' offset field
-      // instead of 36 registers computed once before the loop over pieces)
-      unsigned ql = q_lane;
-      asm volatile("" : "+v"(ql));
+    if constexpr (!T::DQ) return;
+    const char* qb = reinterpret_cast<const char*>(q_ptr) +
+                     ((long long)(bb + jn) * a.s_q * a.h_q + (QG ? 0 : m_lo)) * kRowBytes;
+    const __amdgpu_buffer_rsrc_t qrs = make_rsrc(qb, (QG ? a.s_q * a.h_q : m_hi - m_lo) * kRowBytes);
+    // (opaque, so that the step offsets go into the loads' offset field
+    // instead of registers computed once before the loop over pieces)
+    unsigned ql = q_lane;
+    asm volatile("" : "+v"(ql));
 #pragma unroll
-      for (int ks = 0; ks < T::QREG_STEPS; ++ks)
-        qf[ks] = __builtin_bit_cast(i16x8, __builtin_amdgcn_raw_buffer_load_b128(qrs, ql + 32 * ks, 0, 0));
+    for (int ks = 0; ks < T::QREG_STEPS; ++ks)
+      qf[ks] = __builtin_bit_cast(i16x8, __builtin_amdgcn_raw_buffer_load_b128(qrs, ql + QSTEP * ks, 0, 0));
 #pragma unroll
-      for (int j = 0; j < T::QR_STEPS; ++j)
-        load_lds16_asm<false>(qrs, ql + 32 * (T::QREG_STEPS + j), qr_wave + 1024 * j);
-      q_piece = jn;
-    }
+    for (int j = 0; j < T::QR_STEPS; ++j)
+      load_lds16_asm<false>(qrs, ql + QSTEP * (T::QREG_STEPS + j), qr_wave + 1024 * j);
+    q_piece = jn;
   };
-  if (T::WIDE && lvalid) load_q(lj);  // the first piece with keys
+  // The first piece with keys (q_first) of a DQ tile loads its Q^T before
+  // the first two stream positions in WIDE tiles, and between them in the
+  // others (at the start of the piece; see the wait there).
+  const int q_first = lvalid ? lj : -1;
+  constexpr bool Q_BETWEEN = T::DQ && !T::WIDE;
+  if (T::WIDE && q_first >= 0) load_q(q_first);
   plan(lds);
   fire_all();
-  plan(lds + kStageBytes);
-  fire_all();
+  if constexpr (!Q_BETWEEN) {
+    plan(lds + kStageBytes);
+    fire_all();
+  }
 
   int cstage = 0;
   auto slot_of = [&](int c) { return lds + (c & (kSlots - 1)) * kStageBytes; };
@@ -651,10 +672,9 @@ __global__ __launch_bounds__(64 * RG * DG, 1) void decode_kernel(
     wait_vmcnt<LPW>();
     block_barrier();
   };
-  // query rows of this wave inside its query stage
+  // query rows of this wave inside its query stage (tiles with query stages)
   const int q_stage = (rg * R) / kStage;
   const int q_row0 = (rg * R) % kStage;
-
   // Write the normalised output of one piece (scaled by `scale`): out and lse
   // for a whole sequence, else 16-bit partials (and an fp32 lse) for the
   // combine.  Rows leave through LDS: in the MFMA layout a lane holds a few
@@ -1187,15 +1207,30 @@ __global__ __launch_bounds__(64 * RG * DG, 1) void decode_kernel(
     };
 
     if (nst > 0) {
-      // WIDE: a vector-memory wait the compiler can see (a builtin, not asm)
-      // at the start of each piece, while only the piece's Q^T and first two
-      // key stages are in flight (and the previous piece's stores draining).
-      // The Q^T registers are then known to be loaded, and the compiler puts
-      // no wait of its own into the stage loop (there it drained the
-      // prefetched stages in every iteration).
-      if constexpr (T::WIDE) {
-        if (q_piece != j) load_q(j);
-        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+      // A vector-memory wait the compiler can see (a builtin, not asm) at the
+      // start of each piece: the Q^T registers are then known to be loaded,
+      // and the compiler puts no wait of its own into the stage loop (there
+      // it drained the prefetched stages in every iteration).  The first
+      // piece with keys of a tile that is not WIDE issues its Q^T, then
+      // position 1, in straight-line code (the compiler counts these ring
+      // loads, which are builtins), so that only position 1 stays in flight:
+      // its first stage does not wait for position 1.  Every other piece
+      // loaded its Q^T after its first two positions and starts after the
+      // drain at the end of the previous piece (which also keeps the
+      // compiler's view of the loop's back edge free of loads in flight).
+      // Tiles with query stages stream them here (position cstage on).
+      static_assert(LPW < 16, "vmcnt field of the wait below");
+      if constexpr (T::DQ) {
+        if (Q_BETWEEN && j == q_first) {
+          load_q(j);
+          __builtin_amdgcn_sched_barrier(0);  // the Q^T loads stay before position 1's
+          plan(slot_of(cstage + 1));
+          fire_all();
+          __builtin_amdgcn_s_waitcnt(0x0F70 | LPW);  // vmcnt(LPW)
+        } else {
+          if (q_piece != j) load_q(j);
+          __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+        }
       }
       for (int jq = 0; jq < T::NQS; ++jq, ++cstage) {
         stage_ready();
@@ -1206,10 +1241,6 @@ __global__ __launch_bounds__(64 * RG * DG, 1) void decode_kernel(
             const char MLA_LDS* qs = rd + q_row0 * kRowBytes;
 #pragma unroll
             for (int ks = 0; ks < T::QREG_STEPS; ++ks) qf[ks] = lds_read_b128(qs + kstep_off(ks));
-#pragma unroll
-            for (int j = 0; j < T::QR_STEPS; ++j)
-              lds_write_f4(qr0 + 1024 * j,
-                           __builtin_bit_cast(f32x4, lds_read_b128(qs + kstep_off(T::QREG_STEPS + j))));
           }
         }(slot_of(cstage), slot_of(cstage + 2));
       }
@@ -1244,6 +1275,8 @@ __global__ __launch_bounds__(64 * RG * DG, 1) void decode_kernel(
         const char MLA_LDS* xr = xch0 + (T::XCH_BUFS == 2 ? ((s + 1) & 1) * T::XCH_ONE : 0);
         kv_step(Tr{}, Tr{}, slot_of(cstage), slot_of(cstage - 1), xw, xr, s);
       }
+      // The score MFMAs of the piece are done: the next piece's Q^T.
+      if (T::DQ && j + 1 < npieces) load_q(j + 1);
       // drain: the last stage's partials are exchanged; finish it
       block_barrier();
       const char MLA_LDS* xr = xch0 + (T::XCH_BUFS == 2 ? ((nst - 1) & 1) * T::XCH_ONE : 0);
@@ -1277,10 +1310,12 @@ __global__ __launch_bounds__(64 * RG * DG, 1) void decode_kernel(
         def_lse = lse_row;
         def_b = b;
         def_slot = slot;
+        if constexpr (T::DQ) __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): see the start of a piece
         continue;
       }
     }
     write_piece(o, inv, whole, row, lse_row, b, slot);
+    if constexpr (T::DQ) __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): see the start of a piece
   }
   if constexpr (DEFER) {
     if (def_pending) write_piece(o_def, 1.f, def_whole, def_row, def_lse, def_b, def_slot);
