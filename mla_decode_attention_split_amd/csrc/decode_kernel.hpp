@@ -334,6 +334,56 @@ __global__ __launch_bounds__(64 * RG * DG, 1) void decode_kernel(
   const int m_lo = mtile * BM;
   const int m_hi = (m_lo + BM < M ? m_lo + BM : M);  // end of the tile's valid rows
 
+  // ---- lane constants --------------------------------------------------------
+  const int lr = lane % R;  // this lane's query row inside the wave tile
+  const int my_row = m_lo + rg * R + lr;
+  const int q_row = my_row < M ? my_row : M - 1;
+  const int q_t = q_row / hpg;
+  const int q_h = g * hpg + q_row % hpg;
+
+  // Q^T fragments of the current piece (B operands of the score MFMAs).  DQ
+  // tiles load them straight from q into the registers: the wave's local k-step j is
+  // k-step ks = KSPLIT j + kh, and lane l's fragment of it is the 16 bytes of
+  // the lane's query row at dims 16 ks + 8 (l / 32) (R = 32) or
+  // 32 ks + 8 (l / 16) (R = 16), one 16-byte load per k-step.  WIDE tiles
+  // send their rope k-steps into the wave's LDS area by DMA instead, in the
+  // layout they are read in (lane l at 16 l).  Rows past the tile's last
+  // valid row load zeros (outside the buffer's range).  The next piece's Q^T
+  // is loaded right after the current piece's last score MFMAs, so its
+  // latency hides behind the last P V MFMAs and the epilogue, and the ring
+  // carries key stages only.  The 16-row tiles (DQ, not WIDE) load piece 0's
+  // Q^T in the prologue, with the part's page list (Q_EARLY).
+  constexpr int QSTEP = (R == 32 ? 32 : 64) * T::KSPLIT;  // bytes between the wave's k-steps
+  i16x8 qf[T::QREG_STEPS];
+  int q_piece = -1;  // piece whose Q^T is in qf (or in flight)
+  const unsigned q_sub = (unsigned)(R == 32 ? 16 * (lane >> 5) + 32 * kh : 16 * (lane >> 4) + 64 * kh);
+  // The lane's query row in the buffer of the piece's query rows: with one KV
+  // head the tile's rows are consecutive q rows (the buffer starts at the
+  // tile's first row); with several, row m is token m / hpg, head
+  // g hpg + m % hpg of the sequence.
+  const unsigned q_lane =
+      QG ? (my_row < M ? (unsigned)((q_t * a.h_q + q_h) * kRowBytes) + q_sub : kOutOfRange)
+         : (unsigned)((rg * R + lr) * kRowBytes) + q_sub;
+  char MLA_LDS* qr_wave = xch0 + T::XCH_BUFS * T::XCH_ONE + w * T::QR_STEPS * 1024;  // wave-uniform
+  auto load_q = [&](int jn) {
+    if constexpr (!T::DQ) return;
+    const char* qb = reinterpret_cast<const char*>(q_ptr) +
+                     ((long long)(bb + jn) * a.s_q * a.h_q + (QG ? 0 : m_lo)) * kRowBytes;
+    const __amdgpu_buffer_rsrc_t qrs = make_rsrc(qb, (QG ? a.s_q * a.h_q : m_hi - m_lo) * kRowBytes);
+    // (opaque, so that the step offsets go into the loads' offset field
+    // instead of registers computed once before the loop over pieces)
+    unsigned ql = q_lane;
+    asm volatile("" : "+v"(ql));
+#pragma unroll
+    for (int ks = 0; ks < T::QREG_STEPS; ++ks)
+      qf[ks] = __builtin_bit_cast(i16x8, __builtin_amdgcn_raw_buffer_load_b128(qrs, ql + QSTEP * ks, 0, 0));
+#pragma unroll
+    for (int j = 0; j < T::QR_STEPS; ++j)
+      load_lds16_asm<false>(qrs, ql + QSTEP * (T::QREG_STEPS + j), qr_wave + 1024 * j);
+    q_piece = jn;
+  };
+  constexpr bool Q_EARLY = T::DQ && !T::WIDE;
+
   // ---- the part's pages, one per lane --------------------------------------
   // Piece j (sequence bb + j) covers keys [lo_j, hi_j); its pages are entries
   // lo_j / 64 .. ceil(hi_j / 64) - 1 of the sequence's block_table row and
@@ -379,6 +429,7 @@ __global__ __launch_bounds__(64 * RG * DG, 1) void decode_kernel(
   constexpr int LIST_HALVES = T::WIDE ? 1 : 2;
   const bool use_list = !T::WIDE && npieces <= kListPieces && total_listed <= 64 * LIST_HALVES;
   int v_page[LIST_HALVES] = {};
+  if (Q_EARLY) load_q(0);  // (a part's piece 0 has keys unless it ends where it starts)
   if (use_list) {
 #pragma unroll
     for (int half = 0; half < LIST_HALVES; ++half) {
@@ -395,18 +446,12 @@ __global__ __launch_bounds__(64 * RG * DG, 1) void decode_kernel(
       }
       if (idx >= 0) v_page[half] = block_table[idx];
     }
-    // The first position needs the list: wait for it here, where the
-    // compiler sees it (else it finds the list possibly in flight wherever
-    // the stream reads it, and drains the prefetched stages there).
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
   }
+  // The first position needs the list, and piece 0 its Q^T: wait for both
+  // here, where the compiler sees it (else it finds them possibly in flight
+  // wherever the stream reads them, and drains the prefetched stages there).
+  if (Q_EARLY || use_list) __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
 
-  // ---- lane constants --------------------------------------------------------
-  const int lr = lane % R;  // this lane's query row inside the wave tile
-  const int my_row = m_lo + rg * R + lr;
-  const int q_row = my_row < M ? my_row : M - 1;
-  const int q_t = q_row / hpg;
-  const int q_h = g * hpg + q_row % hpg;
 
   // Byte offset (inside a stage) of this lane's k-th 16-byte load, and of the
   // LDS cell it fills (wave w's k-th load fills cells (k NW + w) 64 + lane).
@@ -610,58 +655,13 @@ __global__ __launch_bounds__(64 * RG * DG, 1) void decode_kernel(
       pend = make_rsrc(kv_bytes, 0);
     }
   };
-  // Q^T fragments of the current piece (B operands of the score MFMAs).  DQ
-  // tiles load them straight from q into the registers: the wave's local k-step j is
-  // k-step ks = KSPLIT j + kh, and lane l's fragment of it is the 16 bytes of
-  // the lane's query row at dims 16 ks + 8 (l / 32) (R = 32) or
-  // 32 ks + 8 (l / 16) (R = 16), one 16-byte load per k-step.  WIDE tiles
-  // send their rope k-steps into the wave's LDS area by DMA instead, in the
-  // layout they are read in (lane l at 16 l).  Rows past the tile's last
-  // valid row load zeros (outside the buffer's range).  The next piece's Q^T
-  // is loaded right after the current piece's last score MFMAs, so its
-  // latency hides behind the last P V MFMAs and the epilogue, and the ring
-  // carries key stages only.
-  constexpr int QSTEP = (R == 32 ? 32 : 64) * T::KSPLIT;  // bytes between the wave's k-steps
-  i16x8 qf[T::QREG_STEPS];
-  int q_piece = -1;  // piece whose Q^T is in qf (or in flight)
-  const unsigned q_sub = (unsigned)(R == 32 ? 16 * (lane >> 5) + 32 * kh : 16 * (lane >> 4) + 64 * kh);
-  // The lane's query row in the buffer of the piece's query rows: with one KV
-  // head the tile's rows are consecutive q rows (the buffer starts at the
-  // tile's first row); with several, row m is token m / hpg, head
-  // g hpg + m % hpg of the sequence.
-  const unsigned q_lane =
-      QG ? (my_row < M ? (unsigned)((q_t * a.h_q + q_h) * kRowBytes) + q_sub : kOutOfRange)
-         : (unsigned)((rg * R + lr) * kRowBytes) + q_sub;
-  char MLA_LDS* qr_wave = xch0 + T::XCH_BUFS * T::XCH_ONE + w * T::QR_STEPS * 1024;  // wave-uniform
-  auto load_q = [&](int jn) {
-    if constexpr (!T::DQ) return;
-    const char* qb = reinterpret_cast<const char*>(q_ptr) +
-                     ((long long)(bb + jn) * a.s_q * a.h_q + (QG ? 0 : m_lo)) * kRowBytes;
-    const __amdgpu_buffer_rsrc_t qrs = make_rsrc(qb, (QG ? a.s_q * a.h_q : m_hi - m_lo) * kRowBytes);
-    // (opaque, so that the step offsets go into the loads' offset field
-    // instead of registers computed once before the loop over pieces)
-    unsigned ql = q_lane;
-    asm volatile("" : "+v"(ql));
-#pragma unroll
-    for (int ks = 0; ks < T::QREG_STEPS; ++ks)
-      qf[ks] = __builtin_bit_cast(i16x8, __builtin_amdgcn_raw_buffer_load_b128(qrs, ql + QSTEP * ks, 0, 0));
-#pragma unroll
-    for (int j = 0; j < T::QR_STEPS; ++j)
-      load_lds16_asm<false>(qrs, ql + QSTEP * (T::QREG_STEPS + j), qr_wave + 1024 * j);
-    q_piece = jn;
-  };
-  // The first piece with keys (q_first) of a DQ tile loads its Q^T before
-  // the first two stream positions in WIDE tiles, and between them in the
-  // others (at the start of the piece; see the wait there).
-  const int q_first = lvalid ? lj : -1;
-  constexpr bool Q_BETWEEN = T::DQ && !T::WIDE;
-  if (T::WIDE && q_first >= 0) load_q(q_first);
+  // WIDE tiles load the first piece with keys' Q^T before the first two
+  // stream positions (the 16-row tiles loaded piece 0's with the page list).
+  if (T::WIDE && lvalid) load_q(lj);
   plan(lds);
   fire_all();
-  if constexpr (!Q_BETWEEN) {
-    plan(lds + kStageBytes);
-    fire_all();
-  }
+  plan(lds + kStageBytes);
+  fire_all();
 
   int cstage = 0;
   auto slot_of = [&](int c) { return lds + (c & (kSlots - 1)) * kStageBytes; };
@@ -1207,27 +1207,18 @@ __global__ __launch_bounds__(64 * RG * DG, 1) void decode_kernel(
     };
 
     if (nst > 0) {
-      // A vector-memory wait the compiler can see (a builtin, not asm) at the
-      // start of each piece: the Q^T registers are then known to be loaded,
-      // and the compiler puts no wait of its own into the stage loop (there
-      // it drained the prefetched stages in every iteration).  The first
-      // piece with keys of a tile that is not WIDE issues its Q^T, then
-      // position 1, in straight-line code (the compiler counts these ring
-      // loads, which are builtins), so that only position 1 stays in flight:
-      // its first stage does not wait for position 1.  Every other piece
-      // loaded its Q^T after its first two positions and starts after the
-      // drain at the end of the previous piece (which also keeps the
-      // compiler's view of the loop's back edge free of loads in flight).
-      // Tiles with query stages stream them here (position cstage on).
-      static_assert(LPW < 16, "vmcnt field of the wait below");
+      // DQ tiles: a vector-memory wait the compiler can see (a builtin, not
+      // asm) at the start of each piece: the Q^T registers are then known to
+      // be loaded, and the compiler puts no wait of its own into the stage
+      // loop (there it drained the prefetched stages in every iteration).
+      // Piece 0 of a 16-row tile needs none (its Q^T was waited for with the
+      // page list).  Every later piece loaded its Q^T after its first two
+      // positions and starts after the drain at the end of the previous
+      // piece (which also keeps the compiler's view of the loop's back edge
+      // free of loads in flight).  Tiles with query stages stream them here
+      // (position cstage on).
       if constexpr (T::DQ) {
-        if (Q_BETWEEN && j == q_first) {
-          load_q(j);
-          __builtin_amdgcn_sched_barrier(0);  // the Q^T loads stay before position 1's
-          plan(slot_of(cstage + 1));
-          fire_all();
-          __builtin_amdgcn_s_waitcnt(0x0F70 | LPW);  // vmcnt(LPW)
-        } else {
+        if (!(Q_EARLY && j == 0)) {
           if (q_piece != j) load_q(j);
           __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
         }
