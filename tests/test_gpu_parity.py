@@ -324,6 +324,26 @@ def test_kv_heads_many_rows(h_q, s_q, h_kv):
     check_parity(out, lse, *ref(w), what=f"h_kv={h_kv} M={w.rows_per_kv_head}")
 
 
+@pytest.mark.parametrize("h_q,s_q,h_kv", [(32, 1, 2), (16, 2, 2), (24, 1, 2), (64, 2, 4), (32, 2, 2)])
+@pytest.mark.parametrize("num_parts", [1, 5])
+def test_kv_heads_small_tiles_many_pieces(h_q, s_q, h_kv, num_parts):
+    """Several KV heads with 16- or 32-row tiles, whose query rows are
+    loaded straight into registers through per-lane offsets (row m of a KV
+    head is token m / hpg, head g hpg + m % hpg), reloaded for every piece:
+    parts of many short pieces (some sequences empty), causal when s_q > 1,
+    and a partial row tile (24 heads over 2 KV heads: 12 rows per head)."""
+    rng = np.random.default_rng(30 + h_q + s_q + h_kv + num_parts)
+    lens = rng.integers(0, 300, size=60)
+    lens[rng.integers(0, 60, size=6)] = 0
+    w = synth.make_workload(lens, s_q=s_q, h_q=h_q, h_kv=h_kv, causal=s_q > 1,
+                            seed=31 + h_q + num_parts)
+    case(w, f"h_kv={h_kv} rows {w.rows_per_kv_head}, many pieces, parts={num_parts}")
+    out, lse, meta, _ = run_gpu(w, num_parts=num_parts, return_meta=True)
+    pieces = meta[:, 2] - meta[:, 0] + 1
+    assert pieces.max() > 2, pieces.max()
+    check_parity(out, lse, *ref(w), what=f"h_kv={h_kv} M={w.rows_per_kv_head} parts={num_parts}")
+
+
 def test_pool_past_4gib():
     """Pages at the top of a cache pool larger than 4 GiB (64-bit byte offsets
     of pages): the used pages of a small workload are placed at the pool's
