@@ -14,19 +14,20 @@
 //
 // Design (gfx950):
 //   * One workgroup per CU, 4 waves (one per SIMD).  The part's key stages
-//     (32-key blocks of its pieces) stream through a ring of 4 LDS slots of
-//     36 KB with 16-byte buffer loads straight into LDS.  Every ring position
-//     is loaded with the same number of instructions per wave; lanes with
-//     nothing to load address past their buffer's range, which costs no
-//     memory traffic, so the per-stage waits are exact constants.
+//     (32-key blocks of its pieces; in the 64-row tile also two query stages
+//     per piece) stream through a ring of 4 LDS slots of 36 KB with 16-byte
+//     buffer loads straight into LDS.  Every ring position is loaded with the
+//     same number of instructions per wave; lanes with nothing to load
+//     address past their buffer's range, which costs no memory traffic, so
+//     the per-stage waits are exact constants.
 //   * The prologue needs one memory trip after the part's metadata record:
 //     the record carries the lengths and partial slots of the part's first
 //     and last sequence, and the page indices of the part are loaded into
-//     registers (lane i holds entry i) while the first piece's query rows are
-//     already in flight.
+//     registers (lane i holds entry i) together with the first piece's query
+//     rows.
 //   * Scores are computed transposed, S^T = K Q^T, with K from LDS (A
-//     operand) and Q^T loaded from q straight into registers, where it stays
-//     for the piece (B operand); the MFMA result is
+//     operand) and Q^T in registers for the whole piece (B operand; the 16-
+//     and 128-row tiles load it from q straight into them); the MFMA result is
 //     already laid out as the B operand P^T of O^T = V^T P^T.  V^T comes from
 //     LDS through transposed 8-byte reads (ds_read_b64_tr_b16).
 //   * Tiles of up to 64 rows (split-K): each wave owns R query rows (R = 16
