@@ -37,8 +37,11 @@
  *     mla_decode_noalloc only, a scratch array in device memory that exists
  *     once per GPU for the life of the process.
  *   - `stream` is a hipStream_t (NULL = the default stream).  Compute calls
- *     only enqueue work: they never synchronize with the host and never read
- *     device memory from the host.
+ *     only enqueue work: they never synchronize with the host, never read
+ *     device memory from the host, and enqueue no memset or copy, so a
+ *     sequence of them can be captured in a HIP graph and replayed with new
+ *     contents in the same buffers (the lengths are read on the device
+ *     only).
  *   - Every call returns MLA_OK (0) or a negative status; on failure
  *     nothing has been enqueued unless the status is MLA_ERR_HIP (a launch
  *     error reported by the runtime).  mla_last_error() gives a thread-local
