@@ -122,10 +122,12 @@ int mla_tile_shape(int q_rows_per_kv_head, int h_kv, int *tile_rows, int *m_tile
  * Partition rule (sequences are cut only at multiples of 32 keys), on a
  * cost line counted in half units with f = fixed_cost:
  *   U_b = ceil(N_b / 32); sequence b occupies 2 U_b + 2 f positions (f for
- *   its start, two per unit, f for its end); C_b = sum_{b'<b} (2 U_b' + 2 f);
- *   T = max(2, ceil(C_B / num_parts)).  Unit i of sequence b belongs to part
- *   floor((C_b + f + 2 i + 1) / T) (the part of its midpoint); a sequence
- *   with N_b = 0 gets one empty piece in part floor((C_b + f) / T).  A piece
+ *   its start, two per unit, f for its end); C_b = sum_{b'<b} (2 U_b' + 2 f).
+ *   The parts share the line evenly: position x is in part
+ *   part(x) = floor(x num_parts / C_B), or floor(x / 2) when
+ *   C_B < 2 num_parts.  Unit i of sequence b belongs to part
+ *   part(C_b + f + 2 i + 1) (the part of its midpoint); a sequence with
+ *   N_b = 0 gets one empty piece in part part(C_b + f).  A piece
  *   is the run of one sequence's units inside one part; the pieces of a
  *   sequence sit in consecutive parts.  num_parts and fixed_cost are the
  *   values mla_metadata_shape and mla_tile_shape report.

@@ -108,10 +108,16 @@ int default_partition(int q_rows_per_kv_head, int h_kv, int* num_parts, int* fix
     parts = parts >= 8 ? (parts / 8) * 8 : 8;
     *num_parts = parts;
   }
-  // Per-sequence overhead in 32-key stage units: the query stages of a piece
-  // (one per 32 query rows of the tile) plus about one stage for the
-  // epilogue and the merge of one more piece.
-  if (fixed_cost) *fixed_cost = (tr + 31) / 32 + 1;
+  // Per-sequence overhead in 32-key stage units: the query rows of a piece
+  // (ceil(tile rows / 32) stages' worth) plus about one stage for the
+  // epilogue and the merge of one more piece, and at least 3: the 16- and
+  // 32-row tiles load their query rows straight into registers, but a piece
+  // still costs its prologue's memory trips and its epilogue (3 measured
+  // faster than 2 on every length mix tried with those tiles).
+  if (fixed_cost) {
+    const int f = (tr + 31) / 32 + 1;
+    *fixed_cost = f > 3 ? f : 3;
+  }
   if (tile_rows) *tile_rows = tr;
   if (m_tiles) *m_tiles = mt;
   return MLA_OK;

@@ -12,8 +12,8 @@
 // The kernel is latency-bound (a few hundred integers), so it is built to
 // touch global memory once per input and once per output: cache_seqlens is
 // staged in LDS (up to 4096 sequences), the prefix costs C_b stay in LDS, and each part finds its
-// first and last sequence by binary search with multiplications only (the
-// part of cost position x is floor(x / T), so "part <= p" is "x < (p+1) T").
+// first and last sequence by binary search against the first positions of
+// parts p and p + 1 ("part of x <= p" is "x < first position of p + 1").
 // Integer divisions (software-emulated on the GPU) are only taken a constant
 // number of times per thread.
 //
@@ -21,12 +21,29 @@
 //   C_b = sum over b' < b of (2 U_b' + 2 f)
 //   KF_b = C_b + f + 1 (first unit's midpoint), KL_b = C_b + f + 2 U_b - 1
 //   (last unit's midpoint); both C_b + f for a sequence with no unit.
-//   Part p holds positions [p T, (p+1) T), T = max(2, ceil(C_B / num_parts)).
-//   Units of b before part p: max(0, ceil((p T - C_b - f - 1) / 2)).
+//   The parts share the line evenly: position x is in part
+//   floor(x num_parts / C_B), so part p holds positions [F_p, F_{p+1}) with
+//   F_p = ceil(p C_B / num_parts); when C_B < 2 num_parts every part holds 2
+//   positions instead (part floor(x / 2), F_p = 2 p).
+//   Units of b before part p: max(0, ceil((F_p - C_b - f - 1) / 2)).
 #include "mla_common.hpp"
 #include "mla_internal.hpp"
 
 namespace mla {
+
+// The even share of the cost line among the parts (see the rule above).
+struct PartLine {
+  long long total, parts;
+  __device__ __forceinline__ bool span2() const { return total < 2 * parts; }
+  // part of cost position x >= 0
+  __device__ __forceinline__ long long part_of(long long x) const {
+    return span2() ? x >> 1 : x * parts / total;
+  }
+  // first position of part p (p <= parts)
+  __device__ __forceinline__ long long first_of(long long p) const {
+    return span2() ? 2 * p : (p * total + parts - 1) / parts;
+  }
+};
 
 __device__ __forceinline__ long long units_of(int n) { return ((long long)n + kStage - 1) / kStage; }
 
@@ -88,8 +105,7 @@ __global__ __launch_bounds__(NT) void sched_kernel(const int32_t* __restrict__ s
   }
   long long total;
   long long base = block_exclusive_scan<NT>(local, scratch, &total);
-  long long T = (total + num_parts - 1) / num_parts;
-  if (T < 2) T = 2;
+  const PartLine line{total, num_parts};
 
   // 2. prefix costs, and pieces per sequence = last part - first part + 1.
   long long pieces = 0;
@@ -98,8 +114,8 @@ __global__ __launch_bounds__(NT) void sched_kernel(const int32_t* __restrict__ s
     if (b < batch) {
       C[b] = base;
       const long long u = units_of(SL(b));
-      const long long first = (base + fc + (u > 0 ? 1 : 0)) / T;
-      const long long last = (base + fc + (u > 0 ? 2 * u - 1 : 0)) / T;
+      const long long first = line.part_of(base + fc + (u > 0 ? 1 : 0));
+      const long long last = line.part_of(base + fc + (u > 0 ? 2 * u - 1 : 0));
       pieces += last - first + 1;
       base += 2 * u + 2 * fc;
     }
@@ -114,8 +130,8 @@ __global__ __launch_bounds__(NT) void sched_kernel(const int32_t* __restrict__ s
       if constexpr (kSlInLds) NS_lds[b] = (int32_t)pbase;
       const long long cb = C[b];
       const long long u = units_of(SL(b));
-      const long long first = (cb + fc + (u > 0 ? 1 : 0)) / T;
-      const long long last = (cb + fc + (u > 0 ? 2 * u - 1 : 0)) / T;
+      const long long first = line.part_of(cb + fc + (u > 0 ? 1 : 0));
+      const long long last = line.part_of(cb + fc + (u > 0 ? 2 * u - 1 : 0));
       pbase += last - first + 1;
     }
   }
@@ -127,7 +143,7 @@ __global__ __launch_bounds__(NT) void sched_kernel(const int32_t* __restrict__ s
   __syncthreads();  // C and num_splits complete
 
   // Cost positions that decide a sequence's first and last part:
-  //   last part  = floor(KL_b / T), first part = floor(KF_b / T)
+  //   last part  = part_of(KL_b), first part = part_of(KF_b)
   auto KL = [&](int b) -> long long {
     const long long cb = C[b], u2 = C[b + 1] - cb - 2 * fc;  // 2 U_b
     return cb + fc + (u2 > 0 ? u2 - 1 : 0);
@@ -139,8 +155,8 @@ __global__ __launch_bounds__(NT) void sched_kernel(const int32_t* __restrict__ s
 
   // 3. per part: first sequence with last part >= p, last with first part <= p.
   for (int p = tid; p < num_parts; p += NT) {
-    const long long lo_key = (long long)p * T;         // last part >= p  <=>  KL >= p T
-    const long long hi_key = (long long)(p + 1) * T;   // first part <= p <=>  KF < (p+1) T
+    const long long lo_key = line.first_of(p);       // last part >= p  <=>  KL >= F_p
+    const long long hi_key = line.first_of(p + 1);   // first part <= p <=>  KF < F_{p+1}
     int lo = 0, hi = batch;
     while (lo < hi) {
       const int mid = (lo + hi) >> 1;
@@ -173,7 +189,7 @@ __global__ __launch_bounds__(NT) void sched_kernel(const int32_t* __restrict__ s
       w0 = i32x4{bb, (int32_t)(u_begin * kStage), be, (int32_t)tok_end};
       // partial slot of bb's piece (num_splits[bb] + its split index), both
       // sequence lengths, and the partial slot of be's piece (split 0)
-      w1 = i32x4{NS(bb) + (int32_t)(p - KF(bb) / T), SL(bb), SL(be), NS(be)};
+      w1 = i32x4{NS(bb) + (int32_t)(p - line.part_of(KF(bb))), SL(bb), SL(be), NS(be)};
     }
     i32x4* dst = reinterpret_cast<i32x4*>(meta + (long long)p * kMetaWords);
     dst[0] = w0;
@@ -184,9 +200,7 @@ __global__ __launch_bounds__(NT) void sched_kernel(const int32_t* __restrict__ s
 // Fast variant for up to 1024 sequences and 4096 parts: 256 threads, every
 // per-sequence quantity in LDS.  Each part finds its first and last sequence
 // by binary search over the sequences' last and first parts (both
-// non-decreasing), and the part of a cost position is a multiply by a
-// precomputed reciprocal of T with an exact correction.  Same output as
-// sched_kernel.
+// non-decreasing).  Same output as sched_kernel.
 constexpr int kSmallThreads = 256;
 constexpr int kSmallBatch = 1024;
 constexpr int kSmallParts = 4096;
@@ -213,25 +227,8 @@ __global__ __launch_bounds__(kSmallThreads) void sched_small_kernel(
   }
   long long total;
   long long base = block_exclusive_scan<kSmallThreads>(local, scratch, &total);
-  // positions fit in 31 bits for any realistic batch; 64-bit otherwise
-  const bool narrow = total < 0x7fffffffLL;
-  long long T = narrow ? (long long)(((unsigned)total + (unsigned)num_parts - 1u) / (unsigned)num_parts)
-                       : (total + num_parts - 1) / num_parts;
-  if (T < 2) T = 2;
-  // floor(x / T): q = high half of x * floor((2^32 - 1) / T) is at most 2
-  // below the quotient for x < 2^31; the remainder loop corrects it exactly.
-  const unsigned T32 = (unsigned)T;
-  const unsigned rcp = narrow ? 0xffffffffu / T32 : 0u;
-  auto part_of = [&](long long x) -> int {
-    if (!narrow) return (int)(x / T);
-    unsigned q = __umulhi((unsigned)x, rcp);
-    unsigned r = (unsigned)x - q * T32;
-    while (r >= T32) {
-      ++q;
-      r -= T32;
-    }
-    return (int)q;
-  };
+  const PartLine line{total, num_parts};
+  auto part_of = [&](long long x) -> int { return (int)line.part_of(x); };
   long long pieces = 0;
   for (int i = 0; i < per; ++i) {
     const int b = b0 + i;
@@ -281,7 +278,7 @@ __global__ __launch_bounds__(kSmallThreads) void sched_small_kernel(
     const int be = lo - 1;
     i32x4 w0 = {0, 0, -1, 0}, w1 = {0, 0, 0, 0};
     if (bb < batch && be >= 0 && bb <= be) {
-      const long long lo_key = (long long)p * T, hi_key = (long long)(p + 1) * T;
+      const long long lo_key = line.first_of(p), hi_key = line.first_of(p + 1);
       const long long ub = (C[bb + 1] - C[bb]) / 2 - fc;
       const long long ue = (C[be + 1] - C[be]) / 2 - fc;
       long long u_begin = 0, u_end = 0;

@@ -303,11 +303,14 @@ int mla_oracle_decode_split(const uint16_t *q, const uint16_t *kcache, const int
  *      units, sequence b occupies 2 U_b + 2 f positions: f for its start-up
  *      work, two per unit, f for its finishing work (one fixed cost of f
  *      units per sequence, half at each end).
- *   2. S_b = sum over b' < b of (2 U_b' + 2 f); TOT = S_B.  Every part
- *      spans T = max(2, ceil(TOT / num_parts)) positions: position x belongs
- *      to part floor(x / T).  (T >= 2 puts at least one unit midpoint into
- *      every part that lies inside a sequence's units, so the pieces of a
- *      sequence sit in consecutive parts.)
+ *   2. S_b = sum over b' < b of (2 U_b' + 2 f); TOT = S_B.  The parts
+ *      share the line evenly: position x belongs to part
+ *      floor(x num_parts / TOT), so part p spans positions
+ *      [ceil(p TOT / num_parts), ceil((p + 1) TOT / num_parts)).  When
+ *      TOT < 2 num_parts every part spans 2 positions instead (part
+ *      floor(x / 2)).  (At least 2 positions per part put a unit midpoint
+ *      into every part that lies inside a sequence's units, so the pieces of
+ *      a sequence sit in consecutive parts.)
  *   3. Unit i of sequence b is placed at its midpoint, x = S_b + f + 2 i + 1,
  *      and belongs to that position's part.  A sequence with no unit gets
  *      one empty piece in the part of x = S_b + f.
@@ -324,6 +327,11 @@ int mla_oracle_decode_split(const uint16_t *q, const uint16_t *kcache, const int
  * a scheduler that computes piece bounds arithmetically.
  */
 
+/* The part of cost position x (step 2 above). */
+static long part_of(long x, long tot, long parts) {
+  return tot < 2 * parts ? x / 2 : x * parts / tot;
+}
+
 int mla_oracle_schedule(const int32_t *seqlens, int B, int unit_tokens, int num_parts,
                         int fixed_cost, int32_t *tile_meta, int32_t *num_splits) {
   if (B < 0 || unit_tokens < 1 || num_parts < 1 || fixed_cost < 1) return ORACLE_ERR_ARG;
@@ -338,8 +346,7 @@ int mla_oracle_schedule(const int32_t *seqlens, int B, int unit_tokens, int num_
   const long f = fixed_cost;
   long tot = 0;
   for (int b = 0; b < B; ++b) tot += 2 * (((long)seqlens[b] + unit_tokens - 1) / unit_tokens) + 2 * f;
-  long T = (tot + num_parts - 1) / num_parts;
-  if (T < 2) T = 2;
+  const long P = num_parts;
 
   /* Walk every unit in order; each change of part (or of sequence) starts a
    * new piece.  For every piece remember its sequence, part, split index and
@@ -352,7 +359,7 @@ int mla_oracle_schedule(const int32_t *seqlens, int B, int unit_tokens, int num_
     const long u = (n + unit_tokens - 1) / unit_tokens;
     int split = 0;
     if (u == 0) {
-      const long p = (S + f) / T;
+      const long p = part_of(S + f, tot, P);
       int32_t *w = tile_meta + p * 8;
       if (w[2] < 0) { /* the part's first piece */
         w[0] = b;
@@ -368,7 +375,7 @@ int mla_oracle_schedule(const int32_t *seqlens, int B, int unit_tokens, int num_
     } else {
       long cur = -1;
       for (long i = 0; i < u; ++i) {
-        const long p = (S + f + 2 * i + 1) / T;
+        const long p = part_of(S + f + 2 * i + 1, tot, P);
         const long key_lo = i * unit_tokens;
         const long key_hi = (i + 1) * unit_tokens < n ? (i + 1) * unit_tokens : n;
         int32_t *w = tile_meta + p * 8;

@@ -84,12 +84,13 @@ def test_workspace_size_formula():
 def test_tile_shape_needs_no_device():
     """mla_tile_shape is pure host arithmetic: 16/32/64-row tiles up to 64 rows
     per KV head, 128-row tiles above with one KV head (64-row tiles with
-    several); the default cost is the tile's query stages plus one."""
+    several); the default cost is one stage per 32 tile rows plus one, and at
+    least 3."""
     for M, h_kv, tr in [(1, 1, 16), (16, 1, 16), (17, 1, 32), (32, 1, 32), (33, 1, 64), (64, 1, 64),
                         (65, 1, 128), (256, 1, 128), (4096, 1, 128), (16, 2, 16), (64, 2, 64),
                         (65, 2, 64), (256, 4, 64), (4096, 2, 64)]:
         tile, m_tiles, fixed = mla.mla_tile_shape(M, h_kv)
-        assert (tile, m_tiles, fixed) == (tr, (M + tr - 1) // tr, (tr + 31) // 32 + 1)
+        assert (tile, m_tiles, fixed) == (tr, (M + tr - 1) // tr, max(3, (tr + 31) // 32 + 1))
     with pytest.raises(mla.MlaError):
         mla.mla_tile_shape(0, 1)
     with pytest.raises(mla.MlaError):

@@ -114,7 +114,7 @@ def test_metadata_shape_tiles():
         assert words == 8
         assert tile == tr, (M, tile)
         assert m_tiles == (M + tr - 1) // tr
-        assert fixed == (tr + 31) // 32 + 1
+        assert fixed == max(3, (tr + 31) // 32 + 1)
         per = cus // (m_tiles * h_kv)
         assert parts == (per // 8 * 8 if per >= 8 else 8), (M, h_kv, parts)
         # the default call (no overrides) uses exactly these parameters

@@ -341,18 +341,25 @@ def test_bad_page_index_is_rejected():
 def enumerate_parts(seqlens, num_parts, fixed_cost, unit):
     """Part of every unit, unit by unit, straight from the cost-interval rule:
     a line in half units, each sequence's fixed cost split over its two ends,
-    each unit at its midpoint, parts of T = max(2, ceil(total / num_parts))
-    positions."""
+    each unit at its midpoint, the line shared evenly by the parts (position
+    x in part floor(x num_parts / total), or floor(x / 2) when the line is
+    shorter than two positions per part).  Also returns T, the most
+    positions any part spans."""
     units = [(int(n) + unit - 1) // unit for n in seqlens]
     total = sum(2 * u + 2 * fixed_cost for u in units)
-    T = max(2, -(-total // num_parts))
+    span2 = total < 2 * num_parts
+
+    def part(x):
+        return x // 2 if span2 else x * num_parts // total
+
+    T = 2 if span2 else -(-total // num_parts)
     pos = 0
     where = []
     for u in units:
         if u == 0:
-            where.append([(pos + fixed_cost) // T])
+            where.append([part(pos + fixed_cost)])
         else:
-            where.append([(pos + fixed_cost + 2 * i + 1) // T for i in range(u)])
+            where.append([part(pos + fixed_cost + 2 * i + 1) for i in range(u)])
         pos += 2 * u + 2 * fixed_cost
     return units, where, T
 
@@ -413,7 +420,7 @@ def test_schedule_matches_unit_enumeration(seed):
 @pytest.mark.parametrize("lens,num_parts,fixed_cost", [([32, 0, 64, 100], 256, 1),
                                                         ([1], 1000, 1), ([0, 0, 5000], 64, 3)])
 def test_schedule_tiny_total(lens, num_parts, fixed_cost):
-    """Far more parts than cost positions (T is held at 2 half units): every
+    """Far more parts than cost positions (every part spans 2 half units): every
     sequence's pieces still sit in consecutive parts and cover its keys once."""
     lens = np.asarray(lens)
     meta, ns = oracle.schedule(lens, num_parts=num_parts, fixed_cost=fixed_cost, unit_tokens=32)
@@ -442,6 +449,28 @@ def test_schedule_even_halves():
     for p in range(256):
         b, half = divmod(p, 2)
         assert tuple(meta[p, :4]) == (b, 2048 * half, b, 2048 * (half + 1))
+
+
+@pytest.mark.parametrize("B,num_parts", [(32, 256), (32, 128), (64, 128), (6, 48)])
+@pytest.mark.parametrize("fixed_cost", [1, 2, 3, 4, 5])
+def test_schedule_equal_sequences_whole_groups(B, num_parts, fixed_cost):
+    """The line is shared evenly, so a batch of equal sequences whose count
+    divides the part count splits into whole groups of num_parts / B parts
+    per sequence, for any fixed cost: no part spans two sequences and none is
+    left empty (hand-checked: 32 x 4096 keys, fixed cost 3, 256 parts: each
+    sequence spans 262 half units = 8 parts of 32.75; its first piece ends at
+    the first unit midpoint past 32.75, unit 15, so pieces hold 15, 16, 17,
+    16, 16, 17, 16 and 15 units)."""
+    lens = np.full(B, 4096)
+    meta, ns = oracle.schedule(lens, num_parts=num_parts, fixed_cost=fixed_cost, unit_tokens=32)
+    per = num_parts // B
+    np.testing.assert_array_equal(ns, np.arange(0, num_parts + 1, per))
+    for p in range(num_parts):
+        b = p // per
+        assert meta[p, 0] == b and meta[p, 2] == b, (p, meta[p])
+    if (B, num_parts, fixed_cost) == (32, 256, 3):
+        units = [(int(meta[p, 3]) - int(meta[p, 1])) // 32 for p in range(8)]
+        assert units == [15, 16, 17, 16, 16, 17, 16, 15]
 
 
 def test_schedule_rejects_bad_arguments():
